@@ -1,0 +1,25 @@
+"""CPU oracle for the disentangled-attention forward (float64, numpy).
+
+TEST INFRASTRUCTURE. This package is the slow, plainly written truth that
+the HIP path is checked against. Only `tests/`, `__graft_entry__.smoke()` and
+the `cpu_baseline` leg of `bench.py` may import it. It shares no code with
+the HIP library (no kernels, headers, helpers or tables); the only code both
+sides use is the seeded input generator in `workloads`, which holds none of
+the method's arithmetic.
+
+Modules:
+  bucket    - relative-position bucket and row table, exact integers
+  attention - scores, masked softmax and output per (sequence, head)
+
+Pins (tests marked "not gpu") tie both modules to things other than
+themselves: exact integer identities and invariants of the bucket, a
+pure-Python brute force on tiny inputs, special cases that reduce to
+torch's scaled_dot_product_attention, index-revealing inputs that expose
+which table row each score term reads, a hand-derived worked example
+under tests/golden/, and mask / packing invariants.
+"""
+
+from . import attention, bucket  # noqa: F401
+from .attention import (C2P, P2C, dattn_padded, dattn_rows, dattn_varlen,  # noqa: F401
+                        default_scale)
+from .bucket import log_bucket, rel_index_table, span  # noqa: F401
