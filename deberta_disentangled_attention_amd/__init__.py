@@ -1,0 +1,163 @@
+"""Python binding of libdattn.so (disentangled-attention forward, MI355X).
+
+Argument marshalling only: torch tensors are turned into device pointers,
+element strides and the current HIP stream, and the C entry points of
+include/dattn.h are called by the same names. Every step of the
+computation runs in the library's HIP kernels; there is no Python or CPU
+fallback, and a missing library raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libdattn.so")
+
+DATTN_OK = 0
+DATTN_ERR_INVALID_ARGUMENT = 1
+DATTN_ERR_UNSUPPORTED = 2
+DATTN_ERR_HIP = 3
+DATTN_F32, DATTN_F16, DATTN_BF16 = 0, 1, 2
+DATTN_C2P, DATTN_P2C = 1, 2
+DATTN_MAX_SEQLEN = 8192
+
+_lib_handle = None
+
+
+class DattnError(RuntimeError):
+    def __init__(self, status: int, fn: str):
+        self.status = status
+        super().__init__(f"{fn}: status {status} ({strerror(status)})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libdattn.so (built in-tree by deberta_disentangled_attention_amd.build)."""
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing; build it with "
+                               "`python -m deberta_disentangled_attention_amd.build`")
+        h = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, u32, f32 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                  ctypes.c_uint32, ctypes.c_float)
+        h.rel_bucket.argtypes = [vp, i32, i32, i32, vp]
+        h.rel_bucket.restype = ctypes.c_int
+        h.dattn_fwd_padded.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, i64, i32, vp, i32,
+                                       vp, vp, i32, i32, i32, i32, i32, u32, f32, vp]
+        h.dattn_fwd_padded.restype = ctypes.c_int
+        h.dattn_fwd_varlen.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, i64, i32, vp, i32,
+                                       vp, i32, i32, i64, vp, i32, i32, i32, u32, f32, vp]
+        h.dattn_fwd_varlen.restype = ctypes.c_int
+        h.dattn_strerror.argtypes = [ctypes.c_int]
+        h.dattn_strerror.restype = ctypes.c_char_p
+        _lib_handle = h
+    return _lib_handle
+
+
+def strerror(status: int) -> str:
+    return lib().dattn_strerror(int(status)).decode()
+
+
+def _check(status: int, fn: str) -> None:
+    if status != DATTN_OK:
+        raise DattnError(status, fn)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    return {torch.float32: DATTN_F32, torch.float16: DATTN_F16,
+            torch.bfloat16: DATTN_BF16}.get(t.dtype, -1)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _row_stride(t, name: str) -> int:
+    if t.stride(-1) != 1:
+        raise ValueError(f"{name}: the last dimension must be contiguous")
+    return t.stride(-2)
+
+
+def rel_bucket(max_len: int, position_buckets: int, max_relative_positions: int,
+               *, out=None, device=None):
+    """int32 table of 2*max_len-1 relative rows (see include/dattn.h)."""
+    import torch
+    if out is None:
+        out = torch.empty(2 * max_len - 1, dtype=torch.int32,
+                          device=device if device is not None else "cuda")
+    if out.dtype != torch.int32 or out.numel() < 2 * max_len - 1 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous int32 tensor of 2*max_len-1 entries")
+    _check(lib().rel_bucket(ctypes.c_void_p(out.data_ptr()), max_len, position_buckets,
+                            max_relative_positions, _stream(out)), "rel_bucket")
+    return out
+
+
+def dattn_fwd_padded(q, k, v, qr, kr, rel_idx, rel_max_len: int, mask, H: int, d: int,
+                     *, flags: int = DATTN_C2P | DATTN_P2C, scale: float = 0.0, out=None):
+    """Forward over a padded batch; q, k, v are [B, L, >=H*d] (views of a
+    fused QKV buffer are fine), mask is [B, L] uint8/bool or None."""
+    import torch
+    B, L = q.shape[0], q.shape[1]
+    for name, t in (("k", k), ("v", v)):
+        if t.shape[:2] != q.shape[:2] or t.dtype != q.dtype:
+            raise ValueError(f"{name} must match q in [B, L] and dtype")
+    ld_q, ld_k, ld_v = _row_stride(q, "q"), _row_stride(k, "k"), _row_stride(v, "v")
+    for name, t, ld in (("q", q, ld_q), ("k", k, ld_k), ("v", v, ld_v)):
+        if B > 1 and t.stride(0) != L * ld:
+            raise ValueError(f"{name}: batch stride must be L * row stride")
+    ld_rel = 0
+    if qr is not None:
+        if kr is None or kr.stride() != qr.stride() or kr.shape != qr.shape:
+            raise ValueError("qr and kr must have the same shape and strides")
+        ld_rel = _row_stride(qr, "qr")
+    if mask is not None:
+        if mask.dtype == torch.bool:
+            mask = mask.view(torch.uint8)
+        if mask.dtype != torch.uint8 or not mask.is_contiguous() or tuple(mask.shape) != (B, L):
+            raise ValueError("mask must be a contiguous [B, L] uint8/bool tensor")
+    if out is None:
+        out = torch.empty((B, L, H * d), dtype=q.dtype, device=q.device)
+    n_rel = qr.shape[0] if qr is not None else 0
+    st = lib().dattn_fwd_padded(
+        _ptr(q), _ptr(k), _ptr(v), ld_q, ld_k, ld_v, _ptr(qr), _ptr(kr), ld_rel, n_rel,
+        _ptr(rel_idx), int(rel_max_len), _ptr(mask), _ptr(out), B, L, H, d,
+        _dtype_code(q), int(flags), float(scale), _stream(q))
+    _check(st, "dattn_fwd_padded")
+    return out
+
+
+def dattn_fwd_varlen(q, k, v, qr, kr, rel_idx, rel_max_len: int, cu_seqlens, max_seqlen: int,
+                     H: int, d: int, *, flags: int = DATTN_C2P | DATTN_P2C, scale: float = 0.0,
+                     out=None, total_tokens: Optional[int] = None):
+    """Forward over packed sequences; q, k, v are [total_tokens, >=H*d] and
+    cu_seqlens a device int32 [nseq+1]. max_seqlen (and total_tokens, by
+    default q.shape[0]) are host values."""
+    import torch
+    T = q.shape[0] if total_tokens is None else int(total_tokens)
+    ld_q, ld_k, ld_v = _row_stride(q, "q"), _row_stride(k, "k"), _row_stride(v, "v")
+    if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous int32 tensor")
+    ld_rel = 0
+    if qr is not None:
+        if kr is None or kr.stride() != qr.stride() or kr.shape != qr.shape:
+            raise ValueError("qr and kr must have the same shape and strides")
+        ld_rel = _row_stride(qr, "qr")
+    if out is None:
+        out = torch.empty((q.shape[0], H * d), dtype=q.dtype, device=q.device)
+    n_rel = qr.shape[0] if qr is not None else 0
+    st = lib().dattn_fwd_varlen(
+        _ptr(q), _ptr(k), _ptr(v), ld_q, ld_k, ld_v, _ptr(qr), _ptr(kr), ld_rel, n_rel,
+        _ptr(rel_idx), int(rel_max_len), _ptr(cu_seqlens), cu_seqlens.numel() - 1,
+        int(max_seqlen), T, _ptr(out), H, d, _dtype_code(q), int(flags), float(scale),
+        _stream(q))
+    _check(st, "dattn_fwd_varlen")
+    return out

@@ -1,0 +1,123 @@
+// C ABI of libdattn.so: argument validation and dispatch. Every check runs
+// on the host before any HIP call, so a rejected call touches no device
+// state. There is no fallback path: unsupported cases return a status.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/dattn.h"
+#include "dattn_internal.h"
+
+namespace {
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+int esize_of(int32_t dtype) { return dtype == DATTN_F32 ? 4 : 2; }
+
+// checks shared by both layouts; seq_bound is L (padded) or max_seqlen
+int check_common(const void* q, const void* k, const void* v, int64_t ld_q, int64_t ld_k,
+                 int64_t ld_v, const void* qr, const void* kr, int64_t ld_rel, int32_t n_rel,
+                 const int32_t* rel_idx, int32_t rel_max_len, const void* out, int32_t H,
+                 int32_t d, int32_t dtype, uint32_t flags, float scale, int32_t seq_bound) {
+  if (!q || !k || !v || !out) return DATTN_ERR_INVALID_ARGUMENT;
+  if (H < 1) return DATTN_ERR_INVALID_ARGUMENT;
+  if (flags & ~(DATTN_C2P | DATTN_P2C)) return DATTN_ERR_INVALID_ARGUMENT;
+  if (isnan(scale)) return DATTN_ERR_INVALID_ARGUMENT;
+  if (dtype != DATTN_F32 && dtype != DATTN_F16 && dtype != DATTN_BF16) return DATTN_ERR_UNSUPPORTED;
+  if (d != 32 && d != 64 && d != 128) return DATTN_ERR_UNSUPPORTED;
+  if (seq_bound > DATTN_MAX_SEQLEN) return DATTN_ERR_UNSUPPORTED;
+  const int64_t hd = (int64_t)H * d;
+  if (ld_q < hd || ld_k < hd || ld_v < hd) return DATTN_ERR_INVALID_ARGUMENT;
+  const int es = esize_of(dtype);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return DATTN_ERR_UNSUPPORTED;
+  if ((ld_q * es) % 16 || (ld_k * es) % 16 || (ld_v * es) % 16) return DATTN_ERR_UNSUPPORTED;
+  if (flags) {
+    if (!qr || !kr || !rel_idx) return DATTN_ERR_INVALID_ARGUMENT;
+    if (n_rel < 1 || ld_rel < hd) return DATTN_ERR_INVALID_ARGUMENT;
+    if (rel_max_len < seq_bound || rel_max_len < 1) return DATTN_ERR_INVALID_ARGUMENT;
+    if (!aligned16(qr) || !aligned16(kr) || (ld_rel * es) % 16) return DATTN_ERR_UNSUPPORTED;
+  }
+  return DATTN_OK;
+}
+
+float scale_log2(int32_t d, uint32_t flags, float scale) {
+  const int terms = ((flags & DATTN_C2P) ? 1 : 0) + ((flags & DATTN_P2C) ? 1 : 0);
+  const double tau = scale > 0.f ? (double)scale : 1.0 / sqrt((double)d * (1 + terms));
+  return (float)(tau * 1.4426950408889634);
+}
+
+}  // namespace
+
+extern "C" {
+
+int rel_bucket(int32_t* rel_idx, int32_t max_len, int32_t position_buckets,
+               int32_t max_relative_positions, hipStream_t stream) {
+  if (!rel_idx || max_len < 1) return DATTN_ERR_INVALID_ARGUMENT;
+  if (max_len > 65536) return DATTN_ERR_UNSUPPORTED;
+  if (position_buckets > 0) {
+    const int mid = position_buckets / 2;
+    if (mid < 1) return DATTN_ERR_INVALID_ARGUMENT;
+    if (max_relative_positions - 1 <= mid) return DATTN_ERR_INVALID_ARGUMENT;
+  } else if (max_relative_positions < 1) {
+    return DATTN_ERR_INVALID_ARGUMENT;
+  }
+  return dattn::launch_rel_bucket(rel_idx, max_len, position_buckets, max_relative_positions, stream);
+}
+
+int dattn_fwd_padded(const void* q, const void* k, const void* v, int64_t ld_q, int64_t ld_k,
+                     int64_t ld_v, const void* qr, const void* kr, int64_t ld_rel, int32_t n_rel,
+                     const int32_t* rel_idx, int32_t rel_max_len, const uint8_t* mask, void* out,
+                     int32_t B, int32_t L, int32_t H, int32_t d, int32_t dtype, uint32_t flags,
+                     float scale, hipStream_t stream) {
+  if (B < 0 || L < 0) return DATTN_ERR_INVALID_ARGUMENT;
+  int st = check_common(q, k, v, ld_q, ld_k, ld_v, qr, kr, ld_rel, n_rel, rel_idx, rel_max_len,
+                        out, H, d, dtype, flags, scale, L);
+  if (st != DATTN_OK) return st;
+  if ((int64_t)B * L == 0) return DATTN_OK;
+  dattn::FwdParams p = {};
+  p.q = q; p.k = k; p.v = v;
+  p.ld_q = ld_q; p.ld_k = ld_k; p.ld_v = ld_v;
+  p.qr = qr; p.kr = kr; p.ld_rel = ld_rel; p.n_rel = n_rel;
+  p.rel_idx = rel_idx; p.rel_max_len = rel_max_len;
+  p.mask = mask; p.B = B; p.L = L;
+  p.cu_seqlens = nullptr; p.nseq = 0; p.total_tokens = (int64_t)B * L;
+  p.out = out; p.H = H; p.flags = flags;
+  p.scale_log2 = scale_log2(d, flags, scale);
+  return dattn::launch_fwd(p, dtype, d, false, stream);
+}
+
+int dattn_fwd_varlen(const void* q, const void* k, const void* v, int64_t ld_q, int64_t ld_k,
+                     int64_t ld_v, const void* qr, const void* kr, int64_t ld_rel, int32_t n_rel,
+                     const int32_t* rel_idx, int32_t rel_max_len, const int32_t* cu_seqlens,
+                     int32_t nseq, int32_t max_seqlen, int64_t total_tokens, void* out, int32_t H,
+                     int32_t d, int32_t dtype, uint32_t flags, float scale, hipStream_t stream) {
+  if (nseq < 0 || total_tokens < 0 || max_seqlen < 0) return DATTN_ERR_INVALID_ARGUMENT;
+  if (!cu_seqlens) return DATTN_ERR_INVALID_ARGUMENT;
+  int st = check_common(q, k, v, ld_q, ld_k, ld_v, qr, kr, ld_rel, n_rel, rel_idx, rel_max_len,
+                        out, H, d, dtype, flags, scale, max_seqlen);
+  if (st != DATTN_OK) return st;
+  if (nseq == 0 || total_tokens == 0) return DATTN_OK;
+  dattn::FwdParams p = {};
+  p.q = q; p.k = k; p.v = v;
+  p.ld_q = ld_q; p.ld_k = ld_k; p.ld_v = ld_v;
+  p.qr = qr; p.kr = kr; p.ld_rel = ld_rel; p.n_rel = n_rel;
+  p.rel_idx = rel_idx; p.rel_max_len = rel_max_len;
+  p.mask = nullptr; p.B = 0; p.L = 0;
+  p.cu_seqlens = cu_seqlens; p.nseq = nseq; p.total_tokens = total_tokens;
+  p.out = out; p.H = H; p.flags = flags;
+  p.scale_log2 = scale_log2(d, flags, scale);
+  return dattn::launch_fwd(p, dtype, d, true, stream);
+}
+
+const char* dattn_strerror(int status) {
+  switch (status) {
+    case DATTN_OK: return "ok";
+    case DATTN_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case DATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case DATTN_ERR_HIP: return "HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

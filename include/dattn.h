@@ -1,0 +1,158 @@
+/*
+ * dattn.h - C ABI of libdattn.so, the disentangled-attention forward for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the exact, bidirectional DeBERTa-v2/v3 attention that
+ * DisentangledFlash describes (README "Status": C2P/P2C disentangled
+ * attention, FP16/BF16/strict FP32, head dims 32/64/128, factorised 2-D
+ * padding masks, lengths up to 8192, packed cu_seqlens inference;
+ * kernels-community discussion #31 "Motivation": same operation as the
+ * reference encoder, no approximation, never materialising [B, H, L, L]).
+ * For one sequence and one head, with positions i (query) and j (key):
+ *
+ *   S_ij = scale * ( q_i . k_j
+ *                    + [flags & DATTN_C2P] q_i . kr[T(i - j)]
+ *                    + [flags & DATTN_P2C] k_j . qr[T(j - i)] )
+ *   O_i  = sum_j softmax_j(S_ij over valid keys) v_j
+ *
+ * T is the relative-row table written by rel_bucket(). The pages do not
+ * print these formulas; they are the DeBERTa-v2/v3 definitions the README's
+ * "Attribution" section refers to.
+ *
+ * Conventions shared by every entry point
+ *   - All array pointers are DEVICE pointers, owned by the caller. The
+ *     library allocates nothing, keeps no state between calls and is
+ *     re-entrant; calls on different streams may run concurrently.
+ *   - Every call is asynchronous on `stream` (0 = the null stream) and never
+ *     synchronises with the host. A DATTN_OK return means the work was
+ *     enqueued.
+ *   - Element types (dtype): DATTN_F32, DATTN_F16, DATTN_BF16. q, k, v, qr,
+ *     kr and out all use the same type. Accumulation is in fp32.
+ *   - Head h of a token row occupies columns h*d .. h*d+d-1.
+ *   - Row strides (ld_*) are in elements, must be >= H*d and a multiple of
+ *     16 bytes; every array pointer must be 16-byte aligned. A fused QKV
+ *     buffer [tokens, 3*H*d] is passed as three pointers with ld = 3*H*d.
+ *   - No hidden fallback: an unsupported case returns DATTN_ERR_UNSUPPORTED
+ *     and the caller decides what to do.
+ */
+#ifndef DATTN_H
+#define DATTN_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define DATTN_OK                    0
+#define DATTN_ERR_INVALID_ARGUMENT  1  /* null pointer, bad size, inconsistent lengths */
+#define DATTN_ERR_UNSUPPORTED       2  /* d, dtype, length > 8192, alignment or stride */
+#define DATTN_ERR_HIP               3  /* a HIP launch failed */
+
+/* element types */
+#define DATTN_F32   0
+#define DATTN_F16   1
+#define DATTN_BF16  2
+
+/* position terms (flags bitfield) */
+#define DATTN_C2P   1u   /* content-to-position: q_i . kr[T(i - j)] */
+#define DATTN_P2C   2u   /* position-to-content: k_j . qr[T(j - i)] */
+
+/* longest sequence (the README's bounded kernel families stop at 8192) */
+#define DATTN_MAX_SEQLEN 8192
+
+/*
+ * rel_bucket - write the relative-row table T.
+ *
+ * rel_idx[r + max_len - 1] = clamp(b(r) + s, 0, 2s - 1) for every signed
+ * distance r in [-(max_len-1), max_len-1], i.e. 2*max_len - 1 int32 entries.
+ *   position_buckets > 0 : DeBERTa-v2 log buckets, mid = position_buckets/2,
+ *       b(r) = r for |r| <= mid, else
+ *       sign(r) * (mid + ceil((mid-1) ln(|r|/mid) / ln((M-1)/mid)))
+ *       with M = max_relative_positions; s = position_buckets.
+ *   position_buckets <= 0: no bucketing, b(r) = r, s = max_relative_positions.
+ * The forward then reads 2s rows of qr and kr (n_rel = 2s).
+ * The ceiling is of the real number: the kernel evaluates it in float64 and
+ * settles exact integer values of the argument with integer arithmetic.
+ *
+ * rel_idx : device int32[2*max_len - 1], written.
+ * Errors  : INVALID_ARGUMENT for rel_idx == NULL, max_len < 1, or bucket
+ *           parameters where the formula is undefined (position_buckets == 1,
+ *           or max_relative_positions - 1 <= position_buckets/2 when
+ *           bucketing, or max_relative_positions < 1 without);
+ *           UNSUPPORTED for max_len > 65536; HIP_ERROR if the launch fails.
+ */
+int rel_bucket(int32_t* rel_idx, int32_t max_len, int32_t position_buckets,
+               int32_t max_relative_positions, hipStream_t stream);
+
+/*
+ * dattn_fwd_padded - forward over a right- or arbitrarily-padded batch.
+ *
+ * q, k, v : [B, L, >=H*d] token rows with stride ld_q / ld_k / ld_v elements;
+ *           batch b starts at element b*L*ld.
+ * qr, kr  : [n_rel, >=H*d] projected relative tables, row stride ld_rel,
+ *           shared by the whole batch. May be NULL when flags == 0.
+ * rel_idx : the table from rel_bucket() for max_len = rel_max_len; needs
+ *           rel_max_len >= L. Entries must lie in [0, n_rel); reads are
+ *           clamped into that range. May be NULL when flags == 0.
+ * mask    : [B, L] bytes, nonzero = valid token, or NULL (all valid). It is
+ *           the factorised 2-D mask m_i * m_j: a valid query attends to the
+ *           valid keys only; positions are padded-row indices.
+ * out     : [B, L, H*d], contiguous, written completely: rows of padded
+ *           queries (m_i = 0) are zero.
+ * flags   : DATTN_C2P | DATTN_P2C (0 gives plain softmax attention).
+ * scale   : > 0 overrides the default 1/sqrt(d * (1 + #terms enabled)).
+ *
+ * Errors: INVALID_ARGUMENT (null pointer, B < 0, L < 0, H < 1, ld < H*d,
+ * rel_max_len < L or n_rel < 1 when flags != 0, unknown flag bits, NaN
+ * scale); UNSUPPORTED (d not 32/64/128, unknown dtype, L > 8192,
+ * misaligned pointer or stride); HIP_ERROR. B*L == 0 is a no-op.
+ */
+int dattn_fwd_padded(const void* q, const void* k, const void* v,
+                     int64_t ld_q, int64_t ld_k, int64_t ld_v,
+                     const void* qr, const void* kr, int64_t ld_rel, int32_t n_rel,
+                     const int32_t* rel_idx, int32_t rel_max_len,
+                     const uint8_t* mask, void* out,
+                     int32_t B, int32_t L, int32_t H, int32_t d, int32_t dtype,
+                     uint32_t flags, float scale, hipStream_t stream);
+
+/*
+ * dattn_fwd_varlen - forward over packed sequences (FlashAttention-style
+ * layout: README "Packed unpadded inference"; int32 cumulative lengths as
+ * in the fold-attention README's packed self-attention).
+ *
+ * q, k, v    : [total_tokens, >=H*d] rows with strides ld_q / ld_k / ld_v.
+ * cu_seqlens : device int32[nseq + 1], non-decreasing, cu[0] = 0,
+ *              cu[nseq] = total_tokens. Sequence b is rows cu[b] ..
+ *              cu[b+1]-1; its positions restart at 0. Zero-length
+ *              sequences are allowed. Inconsistent values are undefined
+ *              behaviour, but device reads stay clamped to total_tokens.
+ * max_seqlen : host-side bound on every length (<= 8192, <= rel_max_len
+ *              when flags != 0). nseq, max_seqlen and total_tokens are host
+ *              values, so the call needs no device-to-host read.
+ * out        : [total_tokens, H*d], contiguous; every row is written.
+ * Other arguments as for dattn_fwd_padded.
+ *
+ * Errors: as dattn_fwd_padded, with max_seqlen in place of L; nseq < 0 or
+ * total_tokens < 0 is INVALID_ARGUMENT; nseq == 0 or total_tokens == 0 is
+ * a no-op.
+ */
+int dattn_fwd_varlen(const void* q, const void* k, const void* v,
+                     int64_t ld_q, int64_t ld_k, int64_t ld_v,
+                     const void* qr, const void* kr, int64_t ld_rel, int32_t n_rel,
+                     const int32_t* rel_idx, int32_t rel_max_len,
+                     const int32_t* cu_seqlens, int32_t nseq, int32_t max_seqlen,
+                     int64_t total_tokens, void* out,
+                     int32_t H, int32_t d, int32_t dtype,
+                     uint32_t flags, float scale, hipStream_t stream);
+
+/* Static, human-readable text for a status code. */
+const char* dattn_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DATTN_H */

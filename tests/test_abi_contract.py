@@ -1,0 +1,120 @@
+"""C-ABI contract of libdattn.so, on the CPU.
+
+The library must load and export every function include/dattn.h declares.
+Argument validation runs on the host before any HIP call, so invalid calls
+can be checked here without a GPU: each returns its documented status and
+launches nothing. No compute call is made.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import deberta_disentangled_attention_amd as dd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dattn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(dd.LIB_PATH),
+                                reason="libdattn.so not built")
+
+INV, UNS = dd.DATTN_ERR_INVALID_ARGUMENT, dd.DATTN_ERR_UNSUPPORTED
+A = 4096            # a fake, 16-byte aligned "device address": never dereferenced
+MIS = A + 2         # misaligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert set(names) >= {"rel_bucket", "dattn_fwd_padded", "dattn_fwd_varlen", "dattn_strerror"}
+    h = dd.lib()
+    for n in names:
+        assert hasattr(h, n), n
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    consts = dict(re.findall(r"#define\s+(DATTN_\w+)\s+(\w+)", text))
+    for k, v in consts.items():
+        if k in ("DATTN_H",):
+            continue
+        assert getattr(dd, k) == int(v.rstrip("u")), k
+
+
+def test_strerror():
+    assert dd.strerror(0) == "ok"
+    assert dd.strerror(1) == "invalid argument"
+    assert dd.strerror(2) == "unsupported configuration"
+    assert dd.strerror(3) == "HIP launch failure"
+    assert dd.strerror(99) == "unknown status"
+
+
+def padded(**kw):
+    a = dict(q=A, k=A, v=A, ld_q=768, ld_k=768, ld_v=768, qr=A, kr=A, ld_rel=768, n_rel=512,
+             rel_idx=A, rel_max_len=512, mask=None, out=A, B=2, L=512, H=12, d=64, dtype=2,
+             flags=3, scale=0.0, stream=None)
+    a.update(kw)
+    return dd.lib().dattn_fwd_padded(*a.values())
+
+
+def varlen(**kw):
+    a = dict(q=A, k=A, v=A, ld_q=768, ld_k=768, ld_v=768, qr=A, kr=A, ld_rel=768, n_rel=512,
+             rel_idx=A, rel_max_len=512, cu=A, nseq=2, max_seqlen=512, total=1000, out=A, H=12,
+             d=64, dtype=2, flags=3, scale=0.0, stream=None)
+    a.update(kw)
+    return dd.lib().dattn_fwd_varlen(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INV), (dict(k=None), INV), (dict(v=None), INV), (dict(out=None), INV),
+    (dict(qr=None), INV), (dict(kr=None), INV), (dict(rel_idx=None), INV),
+    (dict(H=0), INV), (dict(B=-1), INV), (dict(L=-1), INV), (dict(ld_q=767), INV),
+    (dict(n_rel=0), INV), (dict(rel_max_len=511), INV), (dict(flags=4), INV),
+    (dict(scale=float("nan")), INV),
+    (dict(d=48), UNS), (dict(d=256), UNS), (dict(dtype=3), UNS), (dict(L=8193, rel_max_len=9000), UNS),
+    (dict(q=MIS), UNS), (dict(out=MIS), UNS), (dict(ld_q=772), UNS), (dict(qr=MIS), UNS),
+    (dict(dtype=0, ld_q=770), UNS),
+])
+def test_padded_rejections(kw, status):
+    assert padded(**kw) == status
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(L=0),
+                                dict(B=0, flags=0, qr=None, kr=None, rel_idx=None)])
+def test_padded_empty_is_noop(kw):
+    assert padded(**kw) == dd.DATTN_OK
+
+
+def test_flags0_needs_no_relative_tables():
+    # still rejected for another reason (d) -> proves the tables were not required
+    assert padded(flags=0, qr=None, kr=None, rel_idx=None, d=48) == UNS
+    assert padded(flags=0, qr=None, kr=None, rel_idx=None, n_rel=0, rel_max_len=0, B=0) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cu=None), INV), (dict(nseq=-1), INV), (dict(total=-1), INV), (dict(max_seqlen=-1), INV),
+    (dict(rel_max_len=100), INV), (dict(max_seqlen=9000, rel_max_len=9000), UNS), (dict(q=None), INV),
+    (dict(d=16), UNS), (dict(k=MIS), UNS),
+])
+def test_varlen_rejections(kw, status):
+    assert varlen(**kw) == status
+
+
+@pytest.mark.parametrize("kw", [dict(nseq=0), dict(total=0)])
+def test_varlen_empty_is_noop(kw):
+    assert varlen(**kw) == dd.DATTN_OK
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, 10, 256, 512), INV), ((A, 0, 256, 512), INV), ((A, 10, 1, 512), INV),
+    ((A, 10, 256, 129), INV), ((A, 10, 0, 0), INV), ((A, 70000, 256, 512), UNS),
+])
+def test_rel_bucket_rejections(args, status):
+    assert dd.lib().rel_bucket(*args, None) == status
