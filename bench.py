@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Benchmark of the disentangled-attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4]
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+the relative-row table (rel_bucket) and the fused forward
+(dattn_fwd_varlen / dattn_fwd_padded), both through the C ABI. Inputs are
+resident in HBM before the timed region. The default workload is the
+long-context packed case: 16 sequences of 8192 tokens (131072 tokens),
+12 heads of 64, bf16, DeBERTa-v2 log buckets 256/512.
+
+Output: one JSON line with the metric (effective TFLOP/s, counting 6*d per
+valid (query, key) pair and head), tokens/s, the roofline object of the
+dominant kernel (the fused forward; its average duration from HIP events
+recorded on the launch stream around each launch) and the CPU oracle timed
+on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "effective TFLOP/s + tokens/s, disentangled attn fwd, bf16 d=64, % MFMA peak"
+PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}   # MI355X dense MFMA
+HBM_GBS = 8000.0
+KERNEL_SOURCES = ["deberta_disentangled_attention_amd/csrc/dattn_fwd.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dattn_fwd_c4_bf16_traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def build_workload(name: str):
+    import workloads
+    table = {
+        "c4": lambda: workloads.c4_long_packed_bf16(),
+        "c2": lambda: workloads.c2_v3base_bf16(),
+        "c3": lambda: workloads.c3_v2xlarge_fp16(),
+        "c3p": lambda: workloads.c3_v2xlarge_fp16(packed=True),
+        "c5d32": lambda: workloads.c5_sweep(32, "bf16"),
+        "c5d128": lambda: workloads.c5_sweep(128, "bf16"),
+        "c5f32": lambda: workloads.c5_sweep(128, "fp32"),
+        "c1": lambda: workloads.c1_tiny_fp32(),
+    }
+    if name not in table:
+        raise SystemExit(f"unknown workload {name}; choose from {sorted(table)}")
+    return table[name]()
+
+
+def describe(w) -> str:
+    lay = "packed" if w.packed else "padded+mask" if w.mask is not None else "padded"
+    bucket = (f"log buckets {w.position_buckets}/{w.max_relative_positions}"
+              if w.position_buckets > 0 else f"identity span {w.max_relative_positions}")
+    return (f"{w.name}: {lay}, B={w.B}, L={w.L}, H={w.H}, d={w.d}, {w.dtype}, {bucket}, "
+            f"{w.total_tokens} valid tokens")
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle baseline (bounded sample, worker processes)
+# ---------------------------------------------------------------------------
+
+def _oracle_unit(args):
+    from threadpoolctl import threadpool_limits
+    import oracle.attention as oa
+    (Qh, Kh, Vh, QRh, KRh, T, relmax, flags, d) = args
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        oa.unit_forward(Qh, Kh, Vh, QRh, KRh, T, relmax, None, flags, oa.default_scale(d, flags))
+        return time.perf_counter() - t0
+
+
+def cpu_baseline(w, max_units: int) -> dict:
+    import multiprocessing as mp
+    import numpy as np
+    import oracle
+    cores = min(len(os.sched_getaffinity(0)), max_units, 16)
+    relmax = w.max_seqlen if w.packed else w.L
+    T = oracle.rel_index_table(relmax, w.position_buckets, w.max_relative_positions)
+    cu = w.cu_seqlens
+    rng = np.random.default_rng(7)
+    order = rng.permutation(w.B * w.H)[:cores]
+    jobs, flop = [], 0.0
+    for u in order:
+        b, h = divmod(int(u), w.H)
+        n = int(w.lens[b])
+        sl = slice(int(cu[b]), int(cu[b + 1])) if w.packed else slice(0, n)
+        src = (lambda x: x[sl]) if w.packed else (lambda x: x[b, sl])
+        col = slice(h * w.d, (h + 1) * w.d)
+        jobs.append((src(w.q)[:, col].astype(np.float64), src(w.k)[:, col].astype(np.float64),
+                     src(w.v)[:, col].astype(np.float64), w.qr[:, col].astype(np.float64),
+                     w.kr[:, col].astype(np.float64), T, relmax, w.flags, w.d))
+        flop += (6 if w.flags else 4) * w.d * float(n) ** 2
+    ctx = mp.get_context("spawn")
+    t0 = time.perf_counter()
+    with ctx.Pool(processes=cores) as pool:
+        pool.map(_oracle_unit, jobs, chunksize=1)
+    wall = time.perf_counter() - t0
+    return {"value": flop / wall / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{len(jobs)} whole (sequence, head) units of {describe(w).split(':')[0]} "
+                      f"({int(w.lens.max())} tokens each at most), float64 numpy oracle, one "
+                      f"single-threaded worker process per unit; wall {wall:.2f} s",
+            "wall_s": wall}
+
+
+# ---------------------------------------------------------------------------
+# GPU timing
+# ---------------------------------------------------------------------------
+
+def load_traffic():
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None          # counters were taken on another version of the kernel
+    return rec.get("traffic_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c4")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-units", type=int, default=16)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import deberta_disentangled_attention_amd as dd
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dd.lib()
+    w = build_workload(args.workload)
+    tdt = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(tdt).cuda()
+    q, k, v, qr, kr = dev(w.q), dev(w.k), dev(w.v), dev(w.qr), dev(w.kr)
+    relmax = w.max_seqlen if w.packed else w.L
+    table = torch.empty(2 * relmax - 1, dtype=torch.int32, device="cuda")
+    if w.packed:
+        cu = torch.from_numpy(w.cu_seqlens).cuda()
+        out = torch.empty((w.total_tokens, w.H * w.d), dtype=tdt, device="cuda")
+    else:
+        mask = None if w.mask is None else torch.from_numpy(w.mask).cuda()
+        out = torch.empty((w.B, w.L, w.H * w.d), dtype=tdt, device="cuda")
+    torch.cuda.synchronize()
+    base_mem = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+
+    def fwd():
+        if w.packed:
+            dd.dattn_fwd_varlen(q, k, v, qr, kr, table, relmax, cu, w.max_seqlen, w.H, w.d,
+                                flags=w.flags, out=out)
+        else:
+            dd.dattn_fwd_padded(q, k, v, qr, kr, table, relmax, mask, w.H, w.d,
+                                flags=w.flags, out=out)
+
+    def step(ev=None):
+        dd.rel_bucket(relmax, w.position_buckets, w.max_relative_positions, out=table)
+        if ev is not None:
+            ev[0].record()
+        fwd()
+        if ev is not None:
+            ev[1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(args.steps):
+        step(events[i])
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t0.elapsed_time(t1)
+    kern_ms = [a.elapsed_time(b) for a, b in events]
+    peak_extra = torch.cuda.max_memory_allocated() - base_mem
+
+    flop = w.effective_flop()
+    ms_per_step = total_ms / args.steps
+    kern_avg_ms = sum(kern_ms) / len(kern_ms)
+    value = flop / (ms_per_step * 1e-3) / 1e12
+    achieved = flop / (kern_avg_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    traffic = load_traffic() if args.workload == "c4" else None
+    res = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded numpy PCG64 inputs of the workload's shape; no dataset, no weights)",
+        "config": {"workload": describe(w), "nseq": w.B, "seq_len": w.L, "heads": w.H,
+                   "head_dim": w.d, "total_tokens": w.total_tokens,
+                   "layout": "packed" if w.packed else "padded",
+                   "position_buckets": w.position_buckets,
+                   "max_relative_positions": w.max_relative_positions,
+                   "flags": w.flags, "parallelism": "single GPU"},
+        "tokens_per_s": round(w.total_tokens / (ms_per_step * 1e-3), 1),
+        "pct_mfma_peak": round(100.0 * value / peak, 2),
+        "effective_flop_per_step": flop,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": traffic,
+                     "kernel": "dattn_fwd_kernel", "kernel_avg_ms": round(kern_avg_ms, 4),
+                     "kernel_min_ms": round(min(kern_ms), 4),
+                     "kernel_max_ms": round(max(kern_ms), 4)},
+        "device_memory": {"peak_extra_bytes_during_steps": int(peak_extra),
+                          "relative_table_bytes": int(table.numel() * 4)},
+        "host_wall_s_timed_region": round(wall, 4),
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_units)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
