@@ -3,39 +3,39 @@
 // What is computed (DisentangledFlash README "Status"; kernels-community
 // discussion #31 "Motivation"): exact bidirectional DeBERTa-v2/v3 attention,
 //   S_ij = tau * (q_i.k_j + q_i.kr[T(i-j)] + k_j.qr[T(j-i)]),
-//   O_i  = softmax over valid keys of S_i. times V,
+//   O_i  = softmax over the valid keys of row i of S, times V,
 // streamed over key tiles with an online softmax so that no [L, L] array is
 // ever stored. T is the relative-row table written by rel_bucket.
 //
 // Work decomposition. One workgroup of NW waves owns BM = 32*NW consecutive
 // queries of one (sequence, head); wave w owns queries 32w .. 32w+31. The
-// workgroup walks the keys in tiles of BN.
+// workgroup walks the keys in tiles of BN, double-buffered through
+// registers: the next tile's K and V rows are in flight from HBM while the
+// current tile is computed from LDS.
 //
 // Orientation. Every score block is produced transposed, S^T = K Q^T, by the
 // 32x32 MFMA (v_mfma_f32_32x32x16_{bf16,f16} or v_mfma_f32_32x32x2_f32). In
 // the MFMA result lane l holds column l%32 and rows 8(r/4) + 4(l/32) + r%4
 // of register r, so each lane owns ONE query and 16 keys of a 32-key block;
 // the lane pair (l, l^32) together hold all keys of that query. Row max and
-// row sum are therefore per-lane scalars with a single cross-half exchange,
-// and P^T is already in the register layout the P.V MFMA (O^T = V^T P^T)
-// takes as its B operand - no transpose of P is needed.
+// row sum are per-lane scalars with a single cross-half exchange, and P^T is
+// already in the register layout the P.V MFMA (O^T = V^T P^T) takes as its
+// B operand - no transpose of P is needed.
 //
-// Position terms. For a tile, the distances i-j span a band of at most
-// 32+BN-1 values per wave and BM+BN-1 per workgroup.
-//  * Band path: the content-to-position products are evaluated for every
-//    distance u of the wave's band, E[u][i] = q_i . kr[T(u)] (MFMA with the
-//    kr rows gathered through T as the A operand), stored in LDS and read
-//    back along the diagonal u = i - j. The position-to-content products
-//    F[j][v] = k_j . qr[T(v)] are evaluated once per workgroup for the
-//    band of v = j - i and read back the same way. Indexing the band by
-//    distance (not by table row) makes every gather address affine in
-//    (i, j), so the read needs no table lookup and no bank conflicts.
-//  * Constant path: once |i - j| is large the table saturates and a term no
-//    longer depends on the pair: C2P becomes a per-query scalar a_i, folded
-//    into the softmax offset, and P2C a per-key scalar c_j, which enters as
-//    the MFMA accumulator input of the Q.K product (c_j = K . qr[T]).
-//    The choice is made per tile from the table values at the band ends
-//    (T is monotone), so it is exact, not a heuristic.
+// Position terms. The relative table is non-decreasing and saturates: beyond
+// the distances sat_top / sat_bot it returns its last / first row. Those two
+// thresholds are found once per workgroup, so the path of a tile is decided
+// by comparing its distance range with them:
+//  * constant path (every pair of the tile reads the same row): C2P is a
+//    per-query scalar a_i = q_i . kr[row], folded into the softmax offset,
+//    and P2C a per-key scalar c_j = k_j . qr[row], computed once per tile
+//    into LDS and fed as the accumulator input of the Q.K MFMA;
+//  * band path: per 32-key half, E[u][i] = q_i . kr[T(u)] for the 63
+//    distances u = i - j of the wave and F[j][v] = k_j . qr[T(v)] for the
+//    BM+31 distances v = j - i of the workgroup are produced by MFMA (table
+//    rows gathered into the A/B operands), stored in LDS and read back along
+//    the diagonal. Indexing the bands by distance makes every gather address
+//    a per-lane base plus a compile-time offset.
 //
 // Masks. The factorised mask m_i m_j: keys with m_j = 0 (or beyond the
 // sequence) get -inf scores and zero V rows; queries with m_i = 0 produce
@@ -102,33 +102,45 @@ template <> struct Ty<TF32> {
 // Compile-time shape of one kernel instance.
 template <class T, int D, int BN, int NW>
 struct Cfg {
-  static constexpr int ESIZE = Ty<T>::ESIZE;
+  static constexpr int ES = Ty<T>::ESIZE;
   static constexpr int NT = 64 * NW;                 // threads
   static constexpr int BM = 32 * NW;                 // queries per workgroup
   static constexpr int NKB = BN / 32;                // 32-key blocks per tile
   static constexpr int NDB = D / 32;                 // 32-wide blocks of the head dim
   static constexpr int HALF = D / 2;                 // reduction elements per lane half
-  static constexpr int NU = HALF * ESIZE / 16;       // 16-byte units per lane half-row
-  static constexpr int EPU = 16 / ESIZE;             // elements per 16-byte unit
+  static constexpr int NU = HALF * ES / 16;          // 16-byte units per lane half-row
+  static constexpr int EPU = 16 / ES;                // elements per 16-byte unit
   static constexpr int NC = HALF / Ty<T>::LANE_K;    // MFMAs per d-long product
-  static constexpr int NBU = BN / 32 + 1;            // C2P band blocks (per wave)
-  static constexpr int NBV = NW + BN / 32;           // P2C band blocks (per workgroup)
+  static constexpr int NBV = NW + 1;                 // F blocks per 32-key half (BM+31 distances)
   static constexpr int KPITCH = D + EPU;             // K tile row pitch (elements)
-  static constexpr int VPITCH = BN + 4;              // V^T tile row pitch (elements)
-  static constexpr int EW = 32 * NBU * 32;           // floats per wave for E
+  // V^T row pitch (elements): an odd number of dwords for 16-bit types keeps
+  // both the transposing stores and the P.V operand reads conflict-free;
+  // fp32 keeps 16-byte alignment for 4-key reads.
+  static constexpr int VPITCH = ES == 2 ? BN + 2 : BN + 4;
+  static constexpr int EW = 64 * 32;                 // floats of E per wave (64 distances x 32 queries)
   static constexpr int FWP = 32 * NBV;               // F row pitch (floats)
-  static constexpr int K_BYTES = BN * KPITCH * ESIZE;
-  static constexpr int V_BYTES = D * VPITCH * ESIZE;
+  static constexpr int UPR = D * ES / 16;            // 16-byte units per K/V row
+  static constexpr int JOBS = (BN / 2) * UPR;        // staging jobs: (row pair, unit)
+  static constexpr int JPT = (JOBS + NT - 1) / NT;   // staging jobs per thread
+  static constexpr int K_BYTES = BN * KPITCH * ES;
+  static constexpr int V_BYTES = (D * VPITCH * ES + 15) / 16 * 16;
   static constexpr int E_BYTES = NW * EW * 4;
-  static constexpr int F_BYTES = BN * FWP * 4;
+  static constexpr int F_BYTES = 32 * FWP * 4;
+  static constexpr int C_BYTES = BN * 4;
+  static constexpr int R_BYTES = 4 * D * ES;         // qr/kr rows at both saturation ends
   static constexpr int OFF_V = K_BYTES;
   static constexpr int OFF_E = OFF_V + V_BYTES;
   static constexpr int OFF_F = OFF_E + E_BYTES;
-  static constexpr int OFF_MISC = OFF_F + F_BYTES;
+  static constexpr int OFF_C = OFF_F + F_BYTES;
+  static constexpr int OFF_R = OFF_C + C_BYTES;
+  static constexpr int OFF_MISC = OFF_R + R_BYTES;
   static constexpr int LDS_BYTES = OFF_MISC + 64;
+  // two workgroups per CU when they fit in its 160 KB of LDS
+  static constexpr int WG_PER_CU = LDS_BYTES <= 80 * 1024 ? 2 : 1;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one CU exceeded");
-  static_assert(NU >= 1 && (HALF * ESIZE) % 16 == 0, "head dim too small");
-  static_assert(K_BYTES % 16 == 0 && V_BYTES % 16 == 0, "alignment");
+  static_assert(NU >= 1 && (HALF * ES) % 16 == 0, "head dim too small");
+  static_assert(K_BYTES % 16 == 0 && (OFF_E % 16) == 0 && (OFF_R % 16) == 0, "alignment");
+  static_assert(BN % 32 == 0 && BN <= 64, "key tile");
 };
 
 // ----------------------------------------------------------------------------
@@ -162,21 +174,59 @@ __device__ __forceinline__ f32x16_t mma_chain(const uint4 (&a)[NU], const uint4 
 }
 
 template <int NU>
-__device__ __forceinline__ void load_half_row(uint4 (&u)[NU], const unsigned char* p, bool ok) {
+__device__ __forceinline__ void load_half_row(uint4 (&u)[NU], const unsigned char* p) {
 #pragma unroll
-  for (int x = 0; x < NU; ++x) u[x] = ok ? ld16(p + 16 * x) : make_uint4(0, 0, 0, 0);
+  for (int x = 0; x < NU; ++x) u[x] = ld16(p + 16 * x);
+}
+
+template <int NU>
+__device__ __forceinline__ void lds_half_row(uint4 (&u)[NU], const unsigned char* p) {
+#pragma unroll
+  for (int x = 0; x < NU; ++x) u[x] = *reinterpret_cast<const uint4*>(p + 16 * x);
 }
 
 __device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32); }
+
+// key offset (within a 32-key block) of accumulator register r in lane half 0
+__device__ __forceinline__ constexpr int rr_of(int r) { return 8 * (r >> 2) + (r & 3); }
+
+// Smallest x in [0, n) with pred(x) true (pred monotone false -> true), or n.
+// Every thread of the workgroup must call it; NT-way parallel search.
+template <int NT, class Pred>
+__device__ int block_first_true(int n, Pred pred, int* slot, int tid) {
+  int lo = -1, hi = n;  // pred(lo) taken false, pred(hi) taken true
+  while (hi - lo > 1) {
+    const int span = hi - lo - 1;
+    const int step = (span + NT - 1) / NT;
+    if (tid == 0) *slot = NT;
+    __syncthreads();
+    const int x = lo + 1 + tid * step;
+    if (x < hi && pred(x)) atomicMin(slot, tid);
+    __syncthreads();
+    const int k = *slot;
+    __syncthreads();
+    if (k == NT) {
+      const int last = min(lo + 1 + (NT - 1) * step, hi - 1);
+      lo = last;
+    } else {
+      hi = lo + 1 + k * step;
+      if (k > 0) lo = lo + 1 + (k - 1) * step;
+    }
+  }
+  return hi;
+}
 
 // ----------------------------------------------------------------------------
 // the kernel
 // ----------------------------------------------------------------------------
 
+enum : int { TERM_OFF = 0, TERM_CONST = 1, TERM_BAND = 2 };
+
 template <class T, int D, int BN, int NW, bool VARLEN>
-__global__ __launch_bounds__(64 * NW) void dattn_fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(64 * NW, (Cfg<T, D, BN, NW>::WG_PER_CU))
+void dattn_fwd_kernel(FwdParams p) {
   typedef Cfg<T, D, BN, NW> C;
-  constexpr int ES = C::ESIZE;
+  constexpr int ES = C::ES;
   constexpr int BM = C::BM;
   constexpr int NT = C::NT;
   constexpr int NU = C::NU;
@@ -186,8 +236,10 @@ __global__ __launch_bounds__(64 * NW) void dattn_fwd_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[C::LDS_BYTES];
   unsigned char* Ks = smem;
   unsigned char* Vt = smem + C::OFF_V;
-  float* Ew_all = reinterpret_cast<float*>(smem + C::OFF_E);
+  float* Ew = reinterpret_cast<float*>(smem + C::OFF_E);
   float* Fw = reinterpret_cast<float*>(smem + C::OFF_F);
+  float* cbuf = reinterpret_cast<float*>(smem + C::OFF_C);
+  unsigned char* Rrows = smem + C::OFF_R;   // qr_top, qr_bot, kr_top, kr_bot
   int* misc = reinterpret_cast<int*>(smem + C::OFF_MISC);
 
   const int tid = threadIdx.x;
@@ -195,7 +247,7 @@ __global__ __launch_bounds__(64 * NW) void dattn_fwd_kernel(FwdParams p) {
   const int wave = tid >> 6;
   const int li = lane & 31;   // query column owned by this lane
   const int lh = lane >> 5;   // lane half: which 4-row groups / which k half
-  float* Ew = Ew_all + wave * C::EW;
+  float* Eww = Ew + wave * C::EW;
 
   // ---- workgroup -> (sequence, head, query tile), XCD-aware ----------------
   // Workgroups are handed to the 8 XCDs round-robin; renumber them so that
@@ -237,18 +289,18 @@ __global__ __launch_bounds__(64 * NW) void dattn_fwd_kernel(FwdParams p) {
       __syncthreads();
       ext = misc[0];
       first_bad = misc[1];
+      __syncthreads();
     } else {
       ext = p.L;
       first_bad = p.L;
     }
     if (qt * BM >= ext) {
       // nothing valid in this query tile: its rows of this head are zero
-      constexpr int UPR = D * ES / 16;
       const int r0 = qt * BM;
       const int nrow = min(BM, p.L - r0);
       unsigned char* o = reinterpret_cast<unsigned char*>(p.out);
-      for (int x = tid; x < nrow * UPR; x += NT) {
-        const int r = x / UPR, u = x - r * UPR;
+      for (int x = tid; x < nrow * C::UPR; x += NT) {
+        const int r = x / C::UPR, u = x - r * C::UPR;
         const int64_t off = ((base + r0 + r) * (int64_t)p.H * D + (int64_t)head * D) * ES + 16 * u;
         *reinterpret_cast<uint4*>(o + off) = make_uint4(0, 0, 0, 0);
       }
@@ -258,33 +310,22 @@ __global__ __launch_bounds__(64 * NW) void dattn_fwd_kernel(FwdParams p) {
     head = logical / p.n_qtiles;
     const int t = logical - head * p.n_qtiles;
     // sequence b owns tile slots [floor(cu[b]/BM) + b, floor(cu[b+1]/BM) + b + 1);
-    // find the last b whose first slot is <= t (256-way parallel search)
-    int lo = 0, hi = p.nseq;
-    while (hi - lo > 1) {
-      const int span = hi - lo;
-      const int step = (span + NT - 1) / NT;
-      if (tid == 0) misc[2] = 0;
-      __syncthreads();
-      const int cand = lo + tid * step;
-      if (cand < hi && tid > 0) {
-        const int64_t c = min((int64_t)p.cu_seqlens[cand], p.total_tokens);
-        if (c / BM + cand <= t) atomicMax(&misc[2], tid);
-      }
-      __syncthreads();
-      const int k = misc[2];
-      __syncthreads();
-      lo = lo + k * step;
-      hi = min(lo + step, hi);
-    }
-    const int b = lo;
-    const int64_t c0 = max((int64_t)0, min((int64_t)p.cu_seqlens[b], p.total_tokens));
-    const int64_t c1 = max(c0, min((int64_t)p.cu_seqlens[b + 1], p.total_tokens));
+    // find the last b whose first slot is <= t, i.e. the first b whose first
+    // slot is > t, minus one
+    const int nb = p.nseq;
+    const int64_t tot = p.total_tokens;
+    const int32_t* cu = p.cu_seqlens;
+    const int first_after = block_first_true<NT>(
+        nb, [&](int b) { return min((int64_t)cu[b], tot) / BM + b > t; }, &misc[2], tid);
+    const int b = max(first_after - 1, 0);
+    const int64_t c0 = max((int64_t)0, min((int64_t)cu[b], tot));
+    const int64_t c1 = max(c0, min((int64_t)cu[b + 1], tot));
     qt = t - (int)(c0 / BM) - b;
     base = c0;
     ext = (int)min(c1 - c0, (int64_t)kMaxSeqLen);
     first_bad = ext;
     row_limit = ext;
-    if (p.nseq <= 0 || qt < 0 || qt * BM >= ext) return;
+    if (qt < 0 || qt * BM >= ext) return;
   }
 
   const int i0 = qt * BM;
@@ -299,25 +340,58 @@ __global__ __launch_bounds__(64 * NW) void dattn_fwd_kernel(FwdParams p) {
   const unsigned char* QRg = reinterpret_cast<const unsigned char*>(p.qr);
   const unsigned char* KRg = reinterpret_cast<const unsigned char*>(p.kr);
 
-  // relative row for a signed distance (clamped reads)
-  const int tbl_hi = 2 * p.rel_max_len - 2;
+  // ---- relative table: saturation thresholds and rows ---------------------
+  const int R = p.rel_max_len;
+  const int tbl_n = 2 * R - 1;
+  auto clamp_row = [&](int r) { return r < 0 ? 0 : (r >= p.n_rel ? p.n_rel - 1 : r); };
   auto rel_row = [&](int dist) -> int {
-    int x = dist + p.rel_max_len - 1;
-    x = x < 0 ? 0 : (x > tbl_hi ? tbl_hi : x);
-    int r = p.rel_idx[x];
-    return r < 0 ? 0 : (r >= p.n_rel ? p.n_rel - 1 : r);
+    int x = dist + R - 1;
+    x = x < 0 ? 0 : (x > tbl_n - 1 ? tbl_n - 1 : x);
+    return clamp_row(p.rel_idx[x]);
   };
-  auto rel_half_row = [&](const unsigned char* tab, int row) -> const unsigned char* {
-    return tab + ((int64_t)row * p.ld_rel + hoff + lh * C::HALF) * ES;
-  };
+  int sat_top = 1 << 30, sat_bot = -(1 << 30);
+  if (has_c2p || has_p2c) {
+    const int32_t* tb = p.rel_idx;
+    const int row_hi = tb[tbl_n - 1], row_lo = tb[0];
+    const int first_top = block_first_true<NT>(tbl_n, [&](int x) { return tb[x] == row_hi; },
+                                               &misc[2], tid);
+    const int first_above_bot = block_first_true<NT>(
+        tbl_n, [&](int x) { return tb[x] != row_lo; }, &misc[2], tid);
+    sat_top = first_top - (R - 1);
+    sat_bot = first_above_bot - 1 - (R - 1);
+    // stage the two saturation rows of qr and kr (this head) in LDS
+    constexpr int RU = D * ES / 16;
+    for (int x = tid; x < 4 * RU; x += NT) {
+      const int which = x / RU, u = x - which * RU;
+      const unsigned char* tab = (which < 2) ? QRg : KRg;
+      const int row = clamp_row((which & 1) ? row_lo : row_hi);
+      *reinterpret_cast<uint4*>(Rrows + which * D * ES + 16 * u) =
+          ld16(tab + ((int64_t)row * p.ld_rel + hoff) * ES + 16 * u);
+    }
+  }
 
   // this lane's query row, half of the head dim (B operand of every product)
   uint4 qf[NU];
   {
     const int qi = i0w + li;
-    const bool ok = qi < ext;
-    const unsigned char* src = Qg + ((base + (ok ? qi : 0)) * p.ld_q + hoff + lh * C::HALF) * ES;
-    load_half_row<NU>(qf, src, ok);
+    if (qi < ext) {
+      load_half_row<NU>(qf, Qg + ((base + qi) * p.ld_q + hoff + lh * C::HALF) * ES);
+    } else {
+#pragma unroll
+      for (int x = 0; x < NU; ++x) qf[x] = make_uint4(0, 0, 0, 0);
+    }
+  }
+
+  __syncthreads();  // saturation rows staged
+
+  // a_i at both saturation ends: kr[row] . q_i with every A row equal
+  float a_top = 0.f, a_bot = 0.f;
+  if (has_c2p) {
+    uint4 rf[NU];
+    lds_half_row<NU>(rf, Rrows + 2 * D * ES + lh * C::HALF * ES);
+    a_top = mma_chain<T, NU, NC>(rf, qf, f32x16_t{})[0];
+    lds_half_row<NU>(rf, Rrows + 3 * D * ES + lh * C::HALF * ES);
+    a_bot = mma_chain<T, NU, NC>(rf, qf, f32x16_t{})[0];
   }
 
   // online-softmax state of this lane's query (shared with lane ^ 32)
@@ -327,164 +401,181 @@ __global__ __launch_bounds__(64 * NW) void dattn_fwd_kernel(FwdParams p) {
 #pragma unroll
   for (int x = 0; x < C::NDB; ++x) o_acc[x] = f32x16_t{};
 
-  // constant-term caches
-  int c2p_row_cached = -1;
-  float a_i = 0.f;            // q_i . kr[row] for the cached row
-  int p2c_row_cached = -1;
-  uint4 qrc[NU];              // qr[row] half-row for the cached row
-#pragma unroll
-  for (int x = 0; x < NU; ++x) qrc[x] = make_uint4(0, 0, 0, 0);
-
   const int key_end = min(ext, first_bad);  // keys below this need no mask test
-
-  // valid query range of the workgroup and of this wave
   const int wg_qlo = i0, wg_qhi = min(i0 + BM, ext) - 1;
   const int w_qlo = i0w, w_qhi = min(i0w + 31, ext - 1);
 
+  // ---- K/V staging through registers --------------------------------------
+  // job x = (row pair, 16-byte unit): rows 2*pr and 2*pr+1, unit u
+  uint4 pk[C::JPT][2], pv[C::JPT][2];
+  auto fetch = [&](int j0) {
+    const bool nm = j0 + BN > key_end;
+#pragma unroll
+    for (int s = 0; s < C::JPT; ++s) {
+      const int x = tid + s * NT;
+      const int pr = x / C::UPR, u = x - pr * C::UPR;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int j = j0 + 2 * pr + h;
+        bool ok = (x < C::JOBS) && j < ext;
+        if (ok && nm && j >= first_bad) ok = mrow[j] != 0;
+        if (ok) {
+          pk[s][h] = ld16(Kg + ((base + j) * p.ld_k + hoff) * ES + 16 * u);
+          pv[s][h] = ld16(Vg + ((base + j) * p.ld_v + hoff) * ES + 16 * u);
+        } else {
+          pk[s][h] = make_uint4(0, 0, 0, 0);
+          pv[s][h] = make_uint4(0, 0, 0, 0);
+        }
+      }
+    }
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int s = 0; s < C::JPT; ++s) {
+      const int x = tid + s * NT;
+      if (x < C::JOBS) {
+        const int pr = x / C::UPR, u = x - pr * C::UPR;
+        *reinterpret_cast<uint4*>(Ks + ((2 * pr) * C::KPITCH) * ES + 16 * u) = pk[s][0];
+        *reinterpret_cast<uint4*>(Ks + ((2 * pr + 1) * C::KPITCH) * ES + 16 * u) = pk[s][1];
+        const uint32_t a4[4] = {pv[s][0].x, pv[s][0].y, pv[s][0].z, pv[s][0].w};
+        const uint32_t b4[4] = {pv[s][1].x, pv[s][1].y, pv[s][1].z, pv[s][1].w};
+        if constexpr (ES == 2) {
+          // element e of both rows -> one dword of V^T row (8u + e)
+          uint32_t* vt = reinterpret_cast<uint32_t*>(Vt);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t lo = (e & 1) ? (a4[e >> 1] >> 16) : (a4[e >> 1] & 0xffffu);
+            const uint32_t hi = (e & 1) ? (b4[e >> 1] & 0xffff0000u) : (b4[e >> 1] << 16);
+            vt[((8 * u + e) * C::VPITCH + 2 * pr) >> 1] = lo | hi;
+          }
+        } else {
+          uint2* vt = reinterpret_cast<uint2*>(Vt);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            vt[((4 * u + e) * C::VPITCH + 2 * pr) >> 1] = make_uint2(a4[e], b4[e]);
+        }
+      }
+    }
+  };
+
+  // per-lane gather bases (see the band writes below)
+  const float* e_base = Eww + (li - 4 * lh + 4) * 32 + li;
+  const float* f_base = Fw + 4 * lh * (C::FWP + 1) + (BM - 1 - 32 * wave - li);
+
+  fetch(0);
   for (int j0 = 0; j0 < ext; j0 += BN) {
     const bool need_mask = j0 + BN > key_end;
+    stage();
+    if (j0 + BN < ext) fetch(j0 + BN);
 
-    // ---- stage K (row-major) and V (transposed) of the key tile ----------
-    {
-      constexpr int UPR = D * ES / 16;   // 16-byte units per key row
-      for (int x = tid; x < BN * UPR; x += NT) {
-        const int r = x / UPR, u = x - r * UPR;
-        const int j = j0 + r;
-        bool ok = j < ext;
-        if (ok && need_mask && j >= first_bad) ok = mrow[j] != 0;
-        uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-        if (ok) {
-          kv = ld16(Kg + ((base + j) * p.ld_k + hoff) * ES + 16 * u);
-          vv = ld16(Vg + ((base + j) * p.ld_v + hoff) * ES + 16 * u);
-        }
-        *reinterpret_cast<uint4*>(Ks + (r * C::KPITCH) * ES + 16 * u) = kv;
-        const int dd0 = u * C::EPU;
-        if (ES == 2) {
-          uint16_t* vt = reinterpret_cast<uint16_t*>(Vt);
-          const uint32_t w4[4] = {vv.x, vv.y, vv.z, vv.w};
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            vt[(dd0 + e) * C::VPITCH + r] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
-        } else {
-          uint32_t* vt = reinterpret_cast<uint32_t*>(Vt);
-          vt[(dd0 + 0) * C::VPITCH + r] = vv.x;
-          vt[(dd0 + 1) * C::VPITCH + r] = vv.y;
-          vt[(dd0 + 2) * C::VPITCH + r] = vv.z;
-          vt[(dd0 + 3) * C::VPITCH + r] = vv.w;
-        }
-      }
-    }
-
-    // ---- choose band or constant path for each position term -------------
-    const int wg_klo = j0, wg_khi = min(j0 + BN, ext) - 1;
-    int p2c_mode = 0;  // 0 off, 1 constant, 2 band
-    int p2c_row = 0;
+    // ---- path of each position term for this tile -----------------------
+    const int k_lo = j0, k_hi = min(j0 + BN, ext) - 1;
+    int p2c_mode = TERM_OFF, p2c_which = 0;   // which: 0 top row, 1 bottom row
     if (has_p2c) {
-      const int r_lo = rel_row(wg_klo - wg_qhi), r_hi = rel_row(wg_khi - wg_qlo);
-      p2c_mode = (r_lo == r_hi) ? 1 : 2;
-      p2c_row = r_lo;
+      if (k_lo - wg_qhi >= sat_top) { p2c_mode = TERM_CONST; p2c_which = 0; }
+      else if (k_hi - wg_qlo <= sat_bot) { p2c_mode = TERM_CONST; p2c_which = 1; }
+      else p2c_mode = TERM_BAND;
     }
-    int c2p_mode = 0;
-    int c2p_row = 0;
+    int c2p_mode = TERM_OFF;
+    float a_off = 0.f;
     if (has_c2p && w_qlo <= w_qhi) {
-      const int r_lo = rel_row(w_qlo - wg_khi), r_hi = rel_row(w_qhi - wg_klo);
-      c2p_mode = (r_lo == r_hi) ? 1 : 2;
-      c2p_row = r_lo;
+      if (w_qlo - k_hi >= sat_top) { c2p_mode = TERM_CONST; a_off = a_top; }
+      else if (w_qhi - k_lo <= sat_bot) { c2p_mode = TERM_CONST; a_off = a_bot; }
+      else c2p_mode = TERM_BAND;
     }
 
-    __syncthreads();  // K / V^T staged
+    __syncthreads();  // K / V^T of this tile staged
 
-    // ---- P2C band: F[j][v] = k_j . qr[T(vmin + v)], shared by the waves ---
-    if (p2c_mode == 2) {
-      const int vmin = j0 - (i0 + BM - 1);
-      for (int blk = wave; blk < C::NKB * C::NBV; blk += NW) {
-        const int kb = blk / C::NBV, vb = blk - kb * C::NBV;
+    if (p2c_mode == TERM_CONST) {
+      // c_j = k_j . qr[row] for the tile's keys: every B column is the same row
+      if (wave < C::NKB) {
+        const int kb = wave;
         uint4 kf[NU], rf[NU];
+        lds_half_row<NU>(kf, Ks + ((kb * 32 + li) * C::KPITCH + lh * C::HALF) * ES);
+        lds_half_row<NU>(rf, Rrows + p2c_which * D * ES + lh * C::HALF * ES);
+        const f32x16_t c = mma_chain<T, NU, NC>(kf, rf, f32x16_t{});
+        if (li == 0) {
 #pragma unroll
-        for (int x = 0; x < NU; ++x)
-          kf[x] = *reinterpret_cast<const uint4*>(Ks + ((kb * 32 + li) * C::KPITCH + lh * C::HALF) * ES + 16 * x);
-        const int row = rel_row(vmin + vb * 32 + li);
-        load_half_row<NU>(rf, rel_half_row(QRg, row), true);
-        f32x16_t acc = mma_chain<T, NU, NC>(kf, rf, f32x16_t{});
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = kb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-          Fw[j * C::FWP + vb * 32 + li] = acc[r];
+          for (int q4 = 0; q4 < 4; ++q4)
+            *reinterpret_cast<f32x4_t*>(cbuf + kb * 32 + 8 * q4 + 4 * lh) =
+                f32x4_t{c[4 * q4], c[4 * q4 + 1], c[4 * q4 + 2], c[4 * q4 + 3]};
         }
       }
+      __syncthreads();
     }
-
-    // ---- C2P band: E[u][i] = kr[T(umin + u)] . q_i, per wave --------------
-    if (c2p_mode == 2) {
-      const int umin = i0w - (j0 + BN - 1);
-#pragma unroll
-      for (int ub = 0; ub < C::NBU; ++ub) {
-        uint4 rf[NU];
-        const int row = rel_row(umin + ub * 32 + li);
-        load_half_row<NU>(rf, rel_half_row(KRg, row), true);
-        f32x16_t acc = mma_chain<T, NU, NC>(rf, qf, f32x16_t{});
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int u = ub * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-          Ew[u * 32 + li] = acc[r];
-        }
-      }
-    } else if (c2p_mode == 1 && c2p_row != c2p_row_cached) {
-      // a_i = kr[row] . q_i: every A row is the same kr row
-      uint4 rf[NU];
-      load_half_row<NU>(rf, rel_half_row(KRg, c2p_row), true);
-      f32x16_t acc = mma_chain<T, NU, NC>(rf, qf, f32x16_t{});
-      a_i = acc[0];
-      c2p_row_cached = c2p_row;
-    }
-    if (p2c_mode == 1 && p2c_row != p2c_row_cached) {
-      load_half_row<NU>(qrc, rel_half_row(QRg, p2c_row), true);
-      p2c_row_cached = p2c_row;
-    }
-
-    __syncthreads();  // F (and E) written
 
     // ---- scores -------------------------------------------------------
     f32x16_t s[C::NKB];
 #pragma unroll
     for (int kb = 0; kb < C::NKB; ++kb) {
       uint4 kf[NU];
+      lds_half_row<NU>(kf, Ks + ((kb * 32 + li) * C::KPITCH + lh * C::HALF) * ES);
+
+      if (p2c_mode == TERM_BAND) {
+        // F[jh][v] = k_(j0+32kb+jh) . qr[T(vmin + v)], v over BM+31 distances
+        const int vmin = (j0 + 32 * kb) - (i0 + BM - 1);
+        for (int vb = wave; vb < C::NBV; vb += NW) {
+          uint4 rf[NU];
+          load_half_row<NU>(rf, QRg + ((int64_t)rel_row(vmin + vb * 32 + li) * p.ld_rel + hoff +
+                                       lh * C::HALF) * ES);
+          const f32x16_t f = mma_chain<T, NU, NC>(kf, rf, f32x16_t{});
 #pragma unroll
-      for (int x = 0; x < NU; ++x)
-        kf[x] = *reinterpret_cast<const uint4*>(Ks + ((kb * 32 + li) * C::KPITCH + lh * C::HALF) * ES + 16 * x);
-      f32x16_t acc = f32x16_t{};
-      if (p2c_mode == 1) acc = mma_chain<T, NU, NC>(kf, qrc, acc);  // c_j in every column
-      acc = mma_chain<T, NU, NC>(kf, qf, acc);
-      if (c2p_mode == 2) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int jj = kb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-          acc[r] += Ew[(li - jj + BN - 1) * 32 + li];
+          for (int r = 0; r < 16; ++r)
+            Fw[(rr_of(r) + 4 * lh) * C::FWP + vb * 32 + li] = f[r];
         }
       }
-      if (p2c_mode == 2) {
+      if (c2p_mode == TERM_BAND) {
+        // E[u][i] = kr[T(umin + u)] . q_i, u over the wave's 63 distances
+        const int umin = i0w - (j0 + 32 * kb + 31);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int jj = kb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-          acc[r] += Fw[jj * C::FWP + (jj - 32 * wave - li + BM - 1)];
+        for (int ub = 0; ub < 2; ++ub) {
+          uint4 rf[NU];
+          load_half_row<NU>(rf, KRg + ((int64_t)rel_row(umin + ub * 32 + li) * p.ld_rel + hoff +
+                                       lh * C::HALF) * ES);
+          const f32x16_t e = mma_chain<T, NU, NC>(rf, qf, f32x16_t{});
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            Eww[(ub * 32 + rr_of(r) + 4 * lh) * 32 + li] = e[r];
         }
+      }
+      if (p2c_mode == TERM_BAND) __syncthreads();  // F complete
+
+      f32x16_t acc;
+      if (p2c_mode == TERM_CONST) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4_t c = *reinterpret_cast<const f32x4_t*>(cbuf + kb * 32 + 8 * q4 + 4 * lh);
+          acc[4 * q4] = c[0]; acc[4 * q4 + 1] = c[1]; acc[4 * q4 + 2] = c[2]; acc[4 * q4 + 3] = c[3];
+        }
+      } else {
+        acc = f32x16_t{};
+      }
+      acc = mma_chain<T, NU, NC>(kf, qf, acc);
+      if (c2p_mode == TERM_BAND) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] += e_base[(27 - rr_of(r)) * 32];
+      }
+      if (p2c_mode == TERM_BAND) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] += f_base[rr_of(r) * (C::FWP + 1)];
       }
       if (need_mask) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int j = j0 + kb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+          const int j = j0 + kb * 32 + rr_of(r) + 4 * lh;
           bool ok = j < ext;
           if (ok && j >= first_bad) ok = mrow[j] != 0;
           if (!ok) acc[r] = NEG_INF;
         }
       }
       s[kb] = acc;
+      if (p2c_mode == TERM_BAND && kb + 1 < C::NKB) __syncthreads();  // F reused
     }
 
     // ---- online softmax (base 2, scale folded) ---------------------------
     {
       const float tl2 = p.scale_log2;
-      const float off = (c2p_mode == 1) ? a_i * tl2 : 0.f;
+      const float off = a_off * tl2;
       float mx = NEG_INF;
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb)
@@ -519,18 +610,16 @@ __global__ __launch_bounds__(64 * NW) void dattn_fwd_kernel(FwdParams p) {
       if constexpr (ES == 2) {
 #pragma unroll
         for (int c2 = 0; c2 < 2; ++c2) {
-          f32x8_t pv;
+          f32x8_t pv8;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) pv[e] = s[kb][8 * c2 + e];
-          const typename Ty<T>::frag pb = Ty<T>::cvt8(pv);
+          for (int e = 0; e < 8; ++e) pv8[e] = s[kb][8 * c2 + e];
+          const typename Ty<T>::frag pb = Ty<T>::cvt8(pv8);
 #pragma unroll
           for (int db = 0; db < C::NDB; ++db) {
-            const uint16_t* vrow = reinterpret_cast<const uint16_t*>(Vt) + (db * 32 + li) * C::VPITCH +
-                                   kb * 32 + 16 * c2 + 4 * lh;
-            const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-            const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
-            const typename Ty<T>::frag va =
-                __builtin_bit_cast(typename Ty<T>::frag, make_uint4(lo.x, lo.y, hi.x, hi.y));
+            const uint32_t* vrow = reinterpret_cast<const uint32_t*>(Vt) +
+                                   (((db * 32 + li) * C::VPITCH + kb * 32 + 16 * c2 + 4 * lh) >> 1);
+            const typename Ty<T>::frag va = __builtin_bit_cast(
+                typename Ty<T>::frag, make_uint4(vrow[0], vrow[1], vrow[4], vrow[5]));
             o_acc[db] = Ty<T>::mma(va, pb, o_acc[db]);
           }
         }
