@@ -141,6 +141,8 @@ def main():
     ap.add_argument("--workload", default="c4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-units", type=int, default=16)
+    ap.add_argument("--flags", type=int, default=None,
+                    help="override the position terms (0 none, 1 C2P, 2 P2C, 3 both)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -158,6 +160,8 @@ def main():
         sys.exit(2)
     dd.lib()
     w = build_workload(args.workload)
+    if args.flags is not None:
+        w.flags = args.flags
     tdt = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
     dev = lambda x: torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(tdt).cuda()
     q, k, v, qr, kr = dev(w.q), dev(w.k), dev(w.v), dev(w.qr), dev(w.kr)

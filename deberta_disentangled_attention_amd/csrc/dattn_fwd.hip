@@ -113,15 +113,17 @@ struct Cfg {
   static constexpr int NC = HALF / Ty<T>::LANE_K;    // MFMAs per d-long product
   static constexpr int NBV = NW + 1;                 // F blocks per 32-key half (BM+31 distances)
   static constexpr int KPITCH = D + EPU;             // K tile row pitch (elements)
-  // V^T row pitch (elements): an odd number of dwords for 16-bit types keeps
-  // both the transposing stores and the P.V operand reads conflict-free;
-  // fp32 keeps 16-byte alignment for 4-key reads.
-  static constexpr int VPITCH = ES == 2 ? BN + 2 : BN + 4;
+  // V^T row pitch (elements): BN+4 keeps the P.V operand reads (8 bytes per
+  // lane for 16-bit types, 16 for fp32) aligned and, with the staging order
+  // below, both the reads and the transposing stores free of bank conflicts.
+  static constexpr int VPITCH = BN + 4;
   static constexpr int EW = 64 * 32;                 // floats of E per wave (64 distances x 32 queries)
   static constexpr int FWP = 32 * NBV;               // F row pitch (floats)
   static constexpr int UPR = D * ES / 16;            // 16-byte units per K/V row
-  static constexpr int JOBS = (BN / 2) * UPR;        // staging jobs: (row pair, unit)
-  static constexpr int JPT = (JOBS + NT - 1) / NT;   // staging jobs per thread
+  // staging: a wave moves 16 row pairs x 4 units per step (one group)
+  static constexpr int UG = UPR / 4;                 // unit groups per row
+  static constexpr int GROUPS = UG * (BN / 32);      // groups per tile
+  static constexpr int GPW = (GROUPS + NW - 1) / NW; // groups per wave
   static constexpr int K_BYTES = BN * KPITCH * ES;
   static constexpr int V_BYTES = (D * VPITCH * ES + 15) / 16 * 16;
   static constexpr int E_BYTES = NW * EW * 4;
@@ -141,6 +143,7 @@ struct Cfg {
   static_assert(NU >= 1 && (HALF * ES) % 16 == 0, "head dim too small");
   static_assert(K_BYTES % 16 == 0 && (OFF_E % 16) == 0 && (OFF_R % 16) == 0, "alignment");
   static_assert(BN % 32 == 0 && BN <= 64, "key tile");
+  static_assert(UPR % 4 == 0, "staging groups");
 };
 
 // ----------------------------------------------------------------------------
@@ -406,18 +409,27 @@ void dattn_fwd_kernel(FwdParams p) {
   const int w_qlo = i0w, w_qhi = min(i0w + 31, ext - 1);
 
   // ---- K/V staging through registers --------------------------------------
-  // job x = (row pair, 16-byte unit): rows 2*pr and 2*pr+1, unit u
-  uint4 pk[C::JPT][2], pv[C::JPT][2];
+  // A wave's step moves one group: row pairs 16*pg + (lane%16), 16-byte unit
+  // 4*ug + lane/16 of both rows. V is written transposed, one dword holding
+  // the same element of the two rows of a pair.
+  uint4 pk[C::GPW][2], pv[C::GPW][2];
+  auto job_of = [&](int s, int& pr, int& u) -> bool {
+    const int g = wave + NW * s;
+    const int ug = g % C::UG, pg = g / C::UG;
+    u = 4 * ug + (lane >> 4);
+    pr = 16 * pg + (lane & 15);
+    return g < C::GROUPS;
+  };
   auto fetch = [&](int j0) {
     const bool nm = j0 + BN > key_end;
 #pragma unroll
-    for (int s = 0; s < C::JPT; ++s) {
-      const int x = tid + s * NT;
-      const int pr = x / C::UPR, u = x - pr * C::UPR;
+    for (int s = 0; s < C::GPW; ++s) {
+      int pr, u;
+      const bool live = job_of(s, pr, u);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int j = j0 + 2 * pr + h;
-        bool ok = (x < C::JOBS) && j < ext;
+        bool ok = live && j < ext;
         if (ok && nm && j >= first_bad) ok = mrow[j] != 0;
         if (ok) {
           pk[s][h] = ld16(Kg + ((base + j) * p.ld_k + hoff) * ES + 16 * u);
@@ -431,10 +443,9 @@ void dattn_fwd_kernel(FwdParams p) {
   };
   auto stage = [&]() {
 #pragma unroll
-    for (int s = 0; s < C::JPT; ++s) {
-      const int x = tid + s * NT;
-      if (x < C::JOBS) {
-        const int pr = x / C::UPR, u = x - pr * C::UPR;
+    for (int s = 0; s < C::GPW; ++s) {
+      int pr, u;
+      if (job_of(s, pr, u)) {
         *reinterpret_cast<uint4*>(Ks + ((2 * pr) * C::KPITCH) * ES + 16 * u) = pk[s][0];
         *reinterpret_cast<uint4*>(Ks + ((2 * pr + 1) * C::KPITCH) * ES + 16 * u) = pk[s][1];
         const uint32_t a4[4] = {pv[s][0].x, pv[s][0].y, pv[s][0].z, pv[s][0].w};
@@ -458,6 +469,8 @@ void dattn_fwd_kernel(FwdParams p) {
     }
   };
 
+  // per-lane V^T operand base: row dd = li of each 32-row block, keys from 4*lh
+  const unsigned char* v_base = Vt + (li * C::VPITCH + 4 * lh) * ES;
   // per-lane gather bases (see the band writes below)
   const float* e_base = Eww + (li - 4 * lh + 4) * 32 + li;
   const float* f_base = Fw + 4 * lh * (C::FWP + 1) + (BM - 1 - 32 * wave - li);
@@ -542,11 +555,11 @@ void dattn_fwd_kernel(FwdParams p) {
 
       f32x16_t acc;
       if (p2c_mode == TERM_CONST) {
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const f32x4_t c = *reinterpret_cast<const f32x4_t*>(cbuf + kb * 32 + 8 * q4 + 4 * lh);
-          acc[4 * q4] = c[0]; acc[4 * q4 + 1] = c[1]; acc[4 * q4 + 2] = c[2]; acc[4 * q4 + 3] = c[3];
-        }
+        const f32x4_t* cb = reinterpret_cast<const f32x4_t*>(cbuf + kb * 32 + 4 * lh);
+        const f32x4_t c0 = cb[0], c1 = cb[2], c2 = cb[4], c3 = cb[6];
+        const f32x8_t c01 = __builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7);
+        const f32x8_t c23 = __builtin_shufflevector(c2, c3, 0, 1, 2, 3, 4, 5, 6, 7);
+        acc = __builtin_shufflevector(c01, c23, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
       } else {
         acc = f32x16_t{};
       }
@@ -572,36 +585,60 @@ void dattn_fwd_kernel(FwdParams p) {
       if (p2c_mode == TERM_BAND && kb + 1 < C::NKB) __syncthreads();  // F reused
     }
 
+    // P for the P.V MFMA, already rounded to the element type (16-bit types)
+    typename Ty<T>::frag pfrag[ES == 2 ? C::NKB : 1][2];
     // ---- online softmax (base 2, scale folded) ---------------------------
+    // The exponent offset m_run is raised only when the tile maximum exceeds
+    // it by more than 8 (so every p <= 2^8), and the accumulators are then
+    // rescaled by alpha. O and l share the offset, so O / l does not depend
+    // on that choice; after the first tile alpha is almost always exactly 1.
+    // The multiply is unconditional: a branch around it makes the register
+    // allocator move the O accumulators every tile, which costs more.
     {
       const float tl2 = p.scale_log2;
       const float off = a_off * tl2;
-      float mx = NEG_INF;
+      float mx4[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+        for (int r = 0; r < 16; r += 4) {
+          mx4[0] = fmaxf(mx4[0], s[kb][r]);
+          mx4[1] = fmaxf(mx4[1], s[kb][r + 1]);
+          mx4[2] = fmaxf(mx4[2], s[kb][r + 2]);
+          mx4[3] = fmaxf(mx4[3], s[kb][r + 3]);
+        }
+      float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
       mx = fmaxf(mx, wave_xor32(mx));
       const float mt = (mx == NEG_INF) ? NEG_INF : fmaf(mx, tl2, off);
-      const float m_new = fmaxf(m_run, mt);
-      const float m_use = (m_new == NEG_INF) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      const float bias = off - m_use;
-      float ps = 0.f;
+      const bool raise = mt > m_run + 8.f;
+      {
+        const float m_new = raise ? mt : m_run;
+        const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+        l_part *= alpha;
+#pragma unroll
+        for (int x = 0; x < C::NDB; ++x) o_acc[x] *= alpha;
+        m_run = m_new;
+      }
+      const float bias = off - (m_run == NEG_INF ? 0.f : m_run);
+      float ps4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(s[kb][r], tl2, bias));
-          s[kb][r] = e;
-          ps += e;
-        }
-      l_part = fmaf(l_part, alpha, ps);
-      if (__any(alpha != 1.f)) {
+        for (int c2 = 0; c2 < 2; ++c2) {
+          f32x8_t e8;
 #pragma unroll
-        for (int x = 0; x < C::NDB; ++x) o_acc[x] *= alpha;
-      }
-      m_run = m_new;
+          for (int e = 0; e < 8; ++e) {
+            const float x = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * c2 + e], tl2, bias));
+            e8[e] = x;
+            ps4[e & 3] += x;
+          }
+          if constexpr (ES == 2) pfrag[kb][c2] = Ty<T>::cvt8(e8);
+          else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s[kb][8 * c2 + e] = e8[e];
+          }
+        }
+      l_part += (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
     }
 
     // ---- O^T += V^T P^T --------------------------------------------------
@@ -610,16 +647,14 @@ void dattn_fwd_kernel(FwdParams p) {
       if constexpr (ES == 2) {
 #pragma unroll
         for (int c2 = 0; c2 < 2; ++c2) {
-          f32x8_t pv8;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pv8[e] = s[kb][8 * c2 + e];
-          const typename Ty<T>::frag pb = Ty<T>::cvt8(pv8);
+          const typename Ty<T>::frag pb = pfrag[kb][c2];
 #pragma unroll
           for (int db = 0; db < C::NDB; ++db) {
-            const uint32_t* vrow = reinterpret_cast<const uint32_t*>(Vt) +
-                                   (((db * 32 + li) * C::VPITCH + kb * 32 + 16 * c2 + 4 * lh) >> 1);
+            const unsigned char* vrow = v_base + (db * 32 * C::VPITCH + kb * 32 + 16 * c2) * ES;
+            const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+            const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
             const typename Ty<T>::frag va = __builtin_bit_cast(
-                typename Ty<T>::frag, make_uint4(vrow[0], vrow[1], vrow[4], vrow[5]));
+                typename Ty<T>::frag, make_uint4(lo.x, lo.y, hi.x, hi.y));
             o_acc[db] = Ty<T>::mma(va, pb, o_acc[db]);
           }
         }
@@ -628,9 +663,8 @@ void dattn_fwd_kernel(FwdParams p) {
         for (int q4 = 0; q4 < 4; ++q4) {
 #pragma unroll
           for (int db = 0; db < C::NDB; ++db) {
-            const float* vrow = reinterpret_cast<const float*>(Vt) + (db * 32 + li) * C::VPITCH +
-                                kb * 32 + 8 * q4 + 4 * lh;
-            const f32x4_t vv = *reinterpret_cast<const f32x4_t*>(vrow);
+            const f32x4_t vv = *reinterpret_cast<const f32x4_t*>(
+                v_base + (db * 32 * C::VPITCH + kb * 32 + 8 * q4) * ES);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
               o_acc[db] = Ty<T>::mma(vv[e], s[kb][4 * q4 + e], o_acc[db]);
