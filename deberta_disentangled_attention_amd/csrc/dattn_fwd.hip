@@ -209,8 +209,9 @@ __device__ int block_first_true(int n, Pred pred, int* slot, int tid) {
     const int k = *slot;
     __syncthreads();
     if (k == NT) {
-      const int last = min(lo + 1 + (NT - 1) * step, hi - 1);
-      lo = last;
+      // every tested candidate is false: continue after the last one tested
+      const int ncand = min(NT, (span + step - 1) / step);
+      lo = lo + 1 + (ncand - 1) * step;
     } else {
       hi = lo + 1 + k * step;
       if (k > 0) lo = lo + 1 + (k - 1) * step;
