@@ -133,7 +133,73 @@ def load_traffic():
     return rec.get("traffic_bytes_per_launch")
 
 
+# ---------------------------------------------------------------------------
+# HBM traffic of the forward from rocprofv3 counters
+# ---------------------------------------------------------------------------
+
+COPY_PROBE_BYTES = 1 << 30
+
+
+def copy_probe():
+    """Three launches of a plain elementwise copy of 1 GiB (read 1 GiB,
+    write 1 GiB), for calibrating FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(f"copy probe: {COPY_PROBE_BYTES} bytes read and written per launch, 3 launches")
+
+
+def _counter_per_dispatch(csv_path, counter, kernel_substr):
+    import csv
+    import collections
+    by = collections.defaultdict(float)
+    with open(csv_path) as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] == counter and kernel_substr in row["Kernel_Name"]:
+                by[int(row["Dispatch_Id"])] += float(row["Counter_Value"])
+    if not by:
+        raise SystemExit(f"{csv_path}: no {counter} rows for kernels matching {kernel_substr!r}")
+    vals = list(by.values())
+    return sum(vals) / len(vals), len(vals)
+
+
+def write_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
+    """Combine four rocprofv3 --pmc runs into the traffic record bench.py
+    reports: forward FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each
+    divided by the same counter's reading per byte of the copy probe."""
+    kf, nf = _counter_per_dispatch(fetch_csv, "FETCH_SIZE", "dattn_fwd_kernel")
+    kw, nw = _counter_per_dispatch(write_csv, "WRITE_SIZE", "dattn_fwd_kernel")
+    cf, _ = _counter_per_dispatch(copy_fetch_csv, "FETCH_SIZE", "MulFunctor")
+    cw, _ = _counter_per_dispatch(copy_write_csv, "WRITE_SIZE", "MulFunctor")
+    f_fetch = cf * 1024.0 / COPY_PROBE_BYTES
+    f_write = cw * 1024.0 / COPY_PROBE_BYTES
+    traffic = kf * 1024.0 / f_fetch + kw * 1024.0 / f_write
+    rec = {
+        "kernel": "dattn_fwd_kernel (16 x 8192 packed bf16, H=12, d=64)",
+        "kernel_source_sha256": kernel_source_hash(),
+        "fetch_kib_per_dispatch": kf, "write_kib_per_dispatch": kw,
+        "dispatches": [nf, nw],
+        "copy_probe_bytes": COPY_PROBE_BYTES,
+        "copy_fetch_kib": cf, "copy_write_kib": cw,
+        "calibration_fetch": f_fetch, "calibration_write": f_write,
+        "traffic_bytes_per_launch": traffic,
+    }
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--write-traffic":
+        write_traffic(*sys.argv[2:6])
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--copy-probe":
+        copy_probe()
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
