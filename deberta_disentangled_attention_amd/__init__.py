@@ -14,7 +14,8 @@ import os
 from typing import Optional
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG_DIR, "libdattn.so")
+# the in-tree build; DATTN_LIB may name another build of the same ABI
+LIB_PATH = os.environ.get("DATTN_LIB") or os.path.join(PKG_DIR, "libdattn.so")
 
 DATTN_OK = 0
 DATTN_ERR_INVALID_ARGUMENT = 1

@@ -40,10 +40,10 @@ def compile_command(out: str = LIB_PATH, extra=()) -> list:
     ]
 
 
-def build(verbose: bool = True) -> str:
+def build(verbose: bool = True, out: str = LIB_PATH, extra=()) -> str:
     """Compile the library (always recompiles) and return its path."""
-    tmp = LIB_PATH + ".tmp"
-    cmd = compile_command(tmp)
+    tmp = out + ".tmp"
+    cmd = compile_command(tmp, extra)
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -54,9 +54,13 @@ def build(verbose: bool = True) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    build()
+    # optional: output path, then extra compiler flags (e.g. -DNAME=VALUE)
+    if len(sys.argv) > 1:
+        build(out=os.path.abspath(sys.argv[1]), extra=sys.argv[2:])
+    else:
+        build()

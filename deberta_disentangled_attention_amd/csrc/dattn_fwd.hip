@@ -28,8 +28,9 @@
 // by comparing its distance range with them:
 //  * constant path (every pair of the tile reads the same row): C2P is a
 //    per-query scalar a_i = q_i . kr[row], folded into the softmax offset,
-//    and P2C a per-key scalar c_j = k_j . qr[row], computed once per tile
-//    into LDS and fed as the accumulator input of the Q.K MFMA;
+//    and P2C a per-key scalar c_j = k_j . qr[row], computed while the key
+//    tile is staged (dot products over the lanes holding each row) and fed
+//    as the accumulator input of the Q.K MFMA;
 //  * band path: per 32-key half, E[u][i] = q_i . kr[T(u)] for the 63
 //    distances u = i - j of the wave and F[j][v] = k_j . qr[T(v)] for the
 //    BM+31 distances v = j - i of the workgroup are produced by MFMA (table
@@ -46,7 +47,11 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "dattn_internal.h"
+
+
 
 namespace dattn {
 
@@ -120,7 +125,9 @@ struct Cfg {
   static constexpr int EW = 64 * 32;                 // floats of E per wave (64 distances x 32 queries)
   static constexpr int FWP = 32 * NBV;               // F row pitch (floats)
   static constexpr int UPR = D * ES / 16;            // 16-byte units per K/V row
-  // staging: a wave moves 16 row pairs x 4 units per step (one group)
+  static constexpr int JOBS = (BN / 2) * UPR;        // staging jobs: (row pair, unit)
+  static constexpr int JPT = (JOBS + NT - 1) / NT;   // jobs per thread
+  // V staging: a wave moves 16 row pairs x 4 units per step (one group)
   static constexpr int UG = UPR / 4;                 // unit groups per row
   static constexpr int GROUPS = UG * (BN / 32);      // groups per tile
   static constexpr int GPW = (GROUPS + NW - 1) / NW; // groups per wave
@@ -143,7 +150,7 @@ struct Cfg {
   static_assert(NU >= 1 && (HALF * ES) % 16 == 0, "head dim too small");
   static_assert(K_BYTES % 16 == 0 && (OFF_E % 16) == 0 && (OFF_R % 16) == 0, "alignment");
   static_assert(BN % 32 == 0 && BN <= 64, "key tile");
-  static_assert(UPR % 4 == 0, "staging groups");
+  static_assert(UPR % 4 == 0 && UPR <= 32 && NT % UPR == 0, "staging groups");
 };
 
 // ----------------------------------------------------------------------------
@@ -189,6 +196,46 @@ __device__ __forceinline__ void lds_half_row(uint4 (&u)[NU], const unsigned char
 }
 
 __device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL,
+                                                             0xf, 0xf, false));
+}
+
+// sum over each aligned group of N consecutive lanes (N = 4, 8, 16 or 32);
+// every lane of a group receives the group's sum
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  x += dpp<0xb1>(x);                       // quad_perm [1,0,3,2]
+  x += dpp<0x4e>(x);                       // quad_perm [2,3,0,1]
+  if constexpr (N >= 8) x += dpp<0x141>(x);   // row_half_mirror
+  if constexpr (N >= 16) x += dpp<0x140>(x);  // row_mirror
+  if constexpr (N >= 32) x += __shfl_xor(x, 16);
+  return x;
+}
+
+// dot product of two 16-byte units (8 bf16 / 8 fp16 / 4 fp32), fp32 accumulate
+template <class T>
+__device__ __forceinline__ float dot16(uint4 a, uint4 b) {
+  const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+  float acc = 0.f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    if constexpr (std::is_same<T, TBF16>::value) {
+      typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, av[t]), __builtin_bit_cast(b2, bv[t]),
+                                            acc, false);
+    } else if constexpr (std::is_same<T, TF16>::value) {
+      typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+      acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, av[t]), __builtin_bit_cast(h2, bv[t]), acc,
+                                   false);
+    } else {
+      acc = fmaf(__builtin_bit_cast(float, av[t]), __builtin_bit_cast(float, bv[t]), acc);
+    }
+  }
+  return acc;
+}
 
 // key offset (within a 32-key block) of accumulator register r in lane half 0
 __device__ __forceinline__ constexpr int rr_of(int r) { return 8 * (r >> 2) + (r & 3); }
@@ -410,45 +457,73 @@ void dattn_fwd_kernel(FwdParams p) {
   const int w_qlo = i0w, w_qhi = min(i0w + 31, ext - 1);
 
   // ---- K/V staging through registers --------------------------------------
-  // A wave's step moves one group: row pairs 16*pg + (lane%16), 16-byte unit
-  // 4*ug + lane/16 of both rows. V is written transposed, one dword holding
-  // the same element of the two rows of a pair.
-  uint4 pk[C::GPW][2], pv[C::GPW][2];
-  auto job_of = [&](int s, int& pr, int& u) -> bool {
+  // K: job x = tid + s*NT covers row pair x / UPR, 16-byte unit x % UPR, so
+  // the UPR lanes of a pair hold whole rows (coalesced loads, and the P2C
+  // constant c_j of a row is a sum over those lanes). V: a wave's step moves
+  // one group, row pairs 16*pg + lane%16 and unit 4*ug + lane/16, whose
+  // transposing dword stores (one dword = the same element of both rows of
+  // a pair) are free of bank conflicts.
+  uint4 pk[C::JPT][2], pv[C::GPW][2];
+  auto vjob_of = [&](int s, int& pr, int& u) -> bool {
     const int g = wave + NW * s;
     const int ug = g % C::UG, pg = g / C::UG;
     u = 4 * ug + (lane >> 4);
     pr = 16 * pg + (lane & 15);
     return g < C::GROUPS;
   };
+  auto key_ok = [&](int j, bool nm) {
+    bool ok = j < ext;
+    if (ok && nm && j >= first_bad) ok = mrow[j] != 0;
+    return ok;
+  };
   auto fetch = [&](int j0) {
     const bool nm = j0 + BN > key_end;
 #pragma unroll
-    for (int s = 0; s < C::GPW; ++s) {
-      int pr, u;
-      const bool live = job_of(s, pr, u);
+    for (int s = 0; s < C::JPT; ++s) {
+      const int x = tid + s * NT;
+      const int pr = x / C::UPR, u = x % C::UPR;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int j = j0 + 2 * pr + h;
-        bool ok = live && j < ext;
-        if (ok && nm && j >= first_bad) ok = mrow[j] != 0;
-        if (ok) {
-          pk[s][h] = ld16(Kg + ((base + j) * p.ld_k + hoff) * ES + 16 * u);
-          pv[s][h] = ld16(Vg + ((base + j) * p.ld_v + hoff) * ES + 16 * u);
-        } else {
-          pk[s][h] = make_uint4(0, 0, 0, 0);
-          pv[s][h] = make_uint4(0, 0, 0, 0);
-        }
+        pk[s][h] = (x < C::JOBS && key_ok(j, nm))
+                       ? ld16(Kg + ((base + j) * p.ld_k + hoff) * ES + 16 * u)
+                       : make_uint4(0, 0, 0, 0);
       }
     }
-  };
-  auto stage = [&]() {
 #pragma unroll
     for (int s = 0; s < C::GPW; ++s) {
       int pr, u;
-      if (job_of(s, pr, u)) {
+      const bool live = vjob_of(s, pr, u);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int j = j0 + 2 * pr + h;
+        pv[s][h] = (live && key_ok(j, nm)) ? ld16(Vg + ((base + j) * p.ld_v + hoff) * ES + 16 * u)
+                                           : make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  // cj_which >= 0: also write c_j = k_j . qr[row] (row: 0 top, 1 bottom) of
+  // the staged keys into cbuf
+  auto stage = [&](int cj_which) {
+#pragma unroll
+    for (int s = 0; s < C::JPT; ++s) {
+      const int x = tid + s * NT;
+      const int pr = x / C::UPR, u = x % C::UPR;
+      if (x < C::JOBS) {
         *reinterpret_cast<uint4*>(Ks + ((2 * pr) * C::KPITCH) * ES + 16 * u) = pk[s][0];
         *reinterpret_cast<uint4*>(Ks + ((2 * pr + 1) * C::KPITCH) * ES + 16 * u) = pk[s][1];
+      }
+      if (cj_which >= 0) {   // uniform; every lane joins the group sums
+        const uint4 r = *reinterpret_cast<const uint4*>(Rrows + cj_which * D * ES + 16 * u);
+        const float c0 = group_sum<C::UPR>(dot16<T>(pk[s][0], r));
+        const float c1 = group_sum<C::UPR>(dot16<T>(pk[s][1], r));
+        if (u == 0 && x < C::JOBS) *reinterpret_cast<float2*>(cbuf + 2 * pr) = make_float2(c0, c1);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < C::GPW; ++s) {
+      int pr, u;
+      if (vjob_of(s, pr, u)) {
         const uint32_t a4[4] = {pv[s][0].x, pv[s][0].y, pv[s][0].z, pv[s][0].w};
         const uint32_t b4[4] = {pv[s][1].x, pv[s][1].y, pv[s][1].z, pv[s][1].w};
         if constexpr (ES == 2) {
@@ -479,8 +554,6 @@ void dattn_fwd_kernel(FwdParams p) {
   fetch(0);
   for (int j0 = 0; j0 < ext; j0 += BN) {
     const bool need_mask = j0 + BN > key_end;
-    stage();
-    if (j0 + BN < ext) fetch(j0 + BN);
 
     // ---- path of each position term for this tile -----------------------
     const int k_lo = j0, k_hi = min(j0 + BN, ext) - 1;
@@ -498,92 +571,99 @@ void dattn_fwd_kernel(FwdParams p) {
       else c2p_mode = TERM_BAND;
     }
 
-    __syncthreads();  // K / V^T of this tile staged
+    stage(p2c_mode == TERM_CONST ? p2c_which : -1);
+    if (j0 + BN < ext) fetch(j0 + BN);
+    __syncthreads();  // K, V^T (and c_j) of this tile staged
 
-    if (p2c_mode == TERM_CONST) {
-      // c_j = k_j . qr[row] for the tile's keys: every B column is the same row
-      if (wave < C::NKB) {
-        const int kb = wave;
-        uint4 kf[NU], rf[NU];
-        lds_half_row<NU>(kf, Ks + ((kb * 32 + li) * C::KPITCH + lh * C::HALF) * ES);
-        lds_half_row<NU>(rf, Rrows + p2c_which * D * ES + lh * C::HALF * ES);
-        const f32x16_t c = mma_chain<T, NU, NC>(kf, rf, f32x16_t{});
-        if (li == 0) {
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4)
-            *reinterpret_cast<f32x4_t*>(cbuf + kb * 32 + 8 * q4 + 4 * lh) =
-                f32x4_t{c[4 * q4], c[4 * q4 + 1], c[4 * q4 + 2], c[4 * q4 + 3]};
-        }
-      }
-      __syncthreads();
-    }
+    // A tile that needs no mask test and takes the constant path (or no
+    // path) for both position terms runs a straight-line body.
+    const bool far_tile = !need_mask && c2p_mode != TERM_BAND && p2c_mode != TERM_BAND;
+
+    // accumulator input of the Q.K product: c_j of the constant P2C path
+    auto c_init = [&](int kb) -> f32x16_t {
+      const f32x4_t* cb = reinterpret_cast<const f32x4_t*>(cbuf + kb * 32 + 4 * lh);
+      const f32x4_t c0 = cb[0], c1 = cb[2], c2 = cb[4], c3 = cb[6];
+      const f32x8_t c01 = __builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7);
+      const f32x8_t c23 = __builtin_shufflevector(c2, c3, 0, 1, 2, 3, 4, 5, 6, 7);
+      return __builtin_shufflevector(c01, c23, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+    };
 
     // ---- scores -------------------------------------------------------
     f32x16_t s[C::NKB];
+    auto far_scores = [&](auto p2c_const) {
+      constexpr bool PC = decltype(p2c_const)::value;
+      uint4 kf[C::NKB][NU];
 #pragma unroll
-    for (int kb = 0; kb < C::NKB; ++kb) {
-      uint4 kf[NU];
-      lds_half_row<NU>(kf, Ks + ((kb * 32 + li) * C::KPITCH + lh * C::HALF) * ES);
+      for (int kb = 0; kb < C::NKB; ++kb)
+        lds_half_row<NU>(kf[kb], Ks + ((kb * 32 + li) * C::KPITCH + lh * C::HALF) * ES);
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb) {
+        f32x16_t acc = f32x16_t{};
+        if constexpr (PC) acc = c_init(kb);
+        s[kb] = mma_chain<T, NU, NC>(kf[kb], qf, acc);
+      }
+    };
 
-      if (p2c_mode == TERM_BAND) {
-        // F[jh][v] = k_(j0+32kb+jh) . qr[T(vmin + v)], v over BM+31 distances
-        const int vmin = (j0 + 32 * kb) - (i0 + BM - 1);
-        for (int vb = wave; vb < C::NBV; vb += NW) {
-          uint4 rf[NU];
-          load_half_row<NU>(rf, QRg + ((int64_t)rel_row(vmin + vb * 32 + li) * p.ld_rel + hoff +
-                                       lh * C::HALF) * ES);
-          const f32x16_t f = mma_chain<T, NU, NC>(kf, rf, f32x16_t{});
+    if (far_tile) {
+      if (p2c_mode == TERM_CONST) far_scores(std::true_type{});
+      else far_scores(std::false_type{});
+    } else {
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            Fw[(rr_of(r) + 4 * lh) * C::FWP + vb * 32 + li] = f[r];
-        }
-      }
-      if (c2p_mode == TERM_BAND) {
-        // E[u][i] = kr[T(umin + u)] . q_i, u over the wave's 63 distances
-        const int umin = i0w - (j0 + 32 * kb + 31);
-#pragma unroll
-        for (int ub = 0; ub < 2; ++ub) {
-          uint4 rf[NU];
-          load_half_row<NU>(rf, KRg + ((int64_t)rel_row(umin + ub * 32 + li) * p.ld_rel + hoff +
-                                       lh * C::HALF) * ES);
-          const f32x16_t e = mma_chain<T, NU, NC>(rf, qf, f32x16_t{});
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            Eww[(ub * 32 + rr_of(r) + 4 * lh) * 32 + li] = e[r];
-        }
-      }
-      if (p2c_mode == TERM_BAND) __syncthreads();  // F complete
+      for (int kb = 0; kb < C::NKB; ++kb) {
+        uint4 kf[NU];
+        lds_half_row<NU>(kf, Ks + ((kb * 32 + li) * C::KPITCH + lh * C::HALF) * ES);
 
-      f32x16_t acc;
-      if (p2c_mode == TERM_CONST) {
-        const f32x4_t* cb = reinterpret_cast<const f32x4_t*>(cbuf + kb * 32 + 4 * lh);
-        const f32x4_t c0 = cb[0], c1 = cb[2], c2 = cb[4], c3 = cb[6];
-        const f32x8_t c01 = __builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7);
-        const f32x8_t c23 = __builtin_shufflevector(c2, c3, 0, 1, 2, 3, 4, 5, 6, 7);
-        acc = __builtin_shufflevector(c01, c23, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
-      } else {
-        acc = f32x16_t{};
-      }
-      acc = mma_chain<T, NU, NC>(kf, qf, acc);
-      if (c2p_mode == TERM_BAND) {
+        if (p2c_mode == TERM_BAND) {
+          // F[jh][v] = k_(j0+32kb+jh) . qr[T(vmin + v)], v over BM+31 distances
+          const int vmin = (j0 + 32 * kb) - (i0 + BM - 1);
+          for (int vb = wave; vb < C::NBV; vb += NW) {
+            uint4 rf[NU];
+            load_half_row<NU>(rf, QRg + ((int64_t)rel_row(vmin + vb * 32 + li) * p.ld_rel + hoff +
+                                         lh * C::HALF) * ES);
+            const f32x16_t f = mma_chain<T, NU, NC>(kf, rf, f32x16_t{});
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] += e_base[(27 - rr_of(r)) * 32];
-      }
-      if (p2c_mode == TERM_BAND) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] += f_base[rr_of(r) * (C::FWP + 1)];
-      }
-      if (need_mask) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = j0 + kb * 32 + rr_of(r) + 4 * lh;
-          bool ok = j < ext;
-          if (ok && j >= first_bad) ok = mrow[j] != 0;
-          if (!ok) acc[r] = NEG_INF;
+            for (int r = 0; r < 16; ++r)
+              Fw[(rr_of(r) + 4 * lh) * C::FWP + vb * 32 + li] = f[r];
+          }
         }
+        if (c2p_mode == TERM_BAND) {
+          // E[u][i] = kr[T(umin + u)] . q_i, u over the wave's 63 distances
+          const int umin = i0w - (j0 + 32 * kb + 31);
+#pragma unroll
+          for (int ub = 0; ub < 2; ++ub) {
+            uint4 rf[NU];
+            load_half_row<NU>(rf, KRg + ((int64_t)rel_row(umin + ub * 32 + li) * p.ld_rel + hoff +
+                                         lh * C::HALF) * ES);
+            const f32x16_t e = mma_chain<T, NU, NC>(rf, qf, f32x16_t{});
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              Eww[(ub * 32 + rr_of(r) + 4 * lh) * 32 + li] = e[r];
+          }
+        }
+        if (p2c_mode == TERM_BAND) __syncthreads();  // F complete
+
+        f32x16_t acc = (p2c_mode == TERM_CONST) ? c_init(kb) : f32x16_t{};
+        acc = mma_chain<T, NU, NC>(kf, qf, acc);
+        if (c2p_mode == TERM_BAND) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[r] += e_base[(27 - rr_of(r)) * 32];
+        }
+        if (p2c_mode == TERM_BAND) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[r] += f_base[rr_of(r) * (C::FWP + 1)];
+        }
+        if (need_mask) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = j0 + kb * 32 + rr_of(r) + 4 * lh;
+            bool ok = j < ext;
+            if (ok && j >= first_bad) ok = mrow[j] != 0;
+            if (!ok) acc[r] = NEG_INF;
+          }
+        }
+        s[kb] = acc;
+        if (p2c_mode == TERM_BAND && kb + 1 < C::NKB) __syncthreads();  // F reused
       }
-      s[kb] = acc;
-      if (p2c_mode == TERM_BAND && kb + 1 < C::NKB) __syncthreads();  // F reused
     }
 
     // P for the P.V MFMA, already rounded to the element type (16-bit types)

@@ -54,6 +54,7 @@ __device__ bool exact_hit(uint32_t a, uint32_t mid, uint32_t Mm1, uint32_t n) {
 // ceil((mid-1) ln(a/mid) / ln((M-1)/mid)) for a > mid
 __device__ int log_offset(int a, int mid, int M) {
   if (mid <= 1) return 0;
+  if (a == M - 1) return mid - 1;  // the argument is exactly mid - 1 there
   const double x = (double)(mid - 1) * log((double)a / (double)mid) /
                    log((double)(M - 1) / (double)mid);
   const double n = rint(x);
