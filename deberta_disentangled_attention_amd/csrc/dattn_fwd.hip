@@ -137,12 +137,15 @@ struct Cfg {
   static constexpr int F_BYTES = 32 * FWP * 4;
   static constexpr int C_BYTES = BN * 4;
   static constexpr int R_BYTES = 4 * D * ES;         // qr/kr rows at both saturation ends
+  static constexpr int TW = 2048;                    // table window staged in LDS (entries)
+  static constexpr int TW_BYTES = TW * 4;
   static constexpr int OFF_V = K_BYTES;
   static constexpr int OFF_E = OFF_V + V_BYTES;
   static constexpr int OFF_F = OFF_E + E_BYTES;
   static constexpr int OFF_C = OFF_F + F_BYTES;
   static constexpr int OFF_R = OFF_C + C_BYTES;
-  static constexpr int OFF_MISC = OFF_R + R_BYTES;
+  static constexpr int OFF_TW = OFF_R + R_BYTES;
+  static constexpr int OFF_MISC = OFF_TW + TW_BYTES;
   static constexpr int LDS_BYTES = OFF_MISC + 64;
   // two workgroups per CU when they fit in its 160 KB of LDS
   static constexpr int WG_PER_CU = LDS_BYTES <= 80 * 1024 ? 2 : 1;
@@ -292,6 +295,7 @@ void dattn_fwd_kernel(FwdParams p) {
   float* cbuf = reinterpret_cast<float*>(smem + C::OFF_C);
   unsigned char* Rrows = smem + C::OFF_R;   // qr_top, qr_bot, kr_top, kr_bot
   int* misc = reinterpret_cast<int*>(smem + C::OFF_MISC);
+  int* Tw = reinterpret_cast<int*>(smem + C::OFF_TW);   // table rows for sat_bot < d < sat_top
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -395,21 +399,38 @@ void dattn_fwd_kernel(FwdParams p) {
   const int R = p.rel_max_len;
   const int tbl_n = 2 * R - 1;
   auto clamp_row = [&](int r) { return r < 0 ? 0 : (r >= p.n_rel ? p.n_rel - 1 : r); };
-  auto rel_row = [&](int dist) -> int {
-    int x = dist + R - 1;
-    x = x < 0 ? 0 : (x > tbl_n - 1 ? tbl_n - 1 : x);
-    return clamp_row(p.rel_idx[x]);
-  };
   int sat_top = 1 << 30, sat_bot = -(1 << 30);
+  int row_hi = 0, row_lo = 0;
+  bool tw_ok = false;
+  // row of qr / kr for a signed distance: beyond the saturation thresholds
+  // the table's end rows, inside them the window staged in LDS (or the
+  // table itself when the window is too long to stage)
+  auto rel_row = [&](int dist) -> int {
+    int r;
+    if (dist <= sat_bot) r = row_lo;
+    else if (dist >= sat_top) r = row_hi;
+    else if (tw_ok) r = Tw[dist - sat_bot - 1];
+    else {
+      int x = dist + R - 1;
+      x = x < 0 ? 0 : (x > tbl_n - 1 ? tbl_n - 1 : x);
+      r = p.rel_idx[x];
+    }
+    return clamp_row(r);
+  };
   if (has_c2p || has_p2c) {
     const int32_t* tb = p.rel_idx;
-    const int row_hi = tb[tbl_n - 1], row_lo = tb[0];
+    row_hi = tb[tbl_n - 1];
+    row_lo = tb[0];
     const int first_top = block_first_true<NT>(tbl_n, [&](int x) { return tb[x] == row_hi; },
                                                &misc[2], tid);
     const int first_above_bot = block_first_true<NT>(
         tbl_n, [&](int x) { return tb[x] != row_lo; }, &misc[2], tid);
     sat_top = first_top - (R - 1);
     sat_bot = first_above_bot - 1 - (R - 1);
+    const int wlen = sat_top - sat_bot - 1;
+    tw_ok = wlen <= C::TW;
+    if (tw_ok)
+      for (int x = tid; x < wlen; x += NT) Tw[x] = tb[sat_bot + 1 + x + R - 1];
     // stage the two saturation rows of qr and kr (this head) in LDS
     constexpr int RU = D * ES / 16;
     for (int x = tid; x < 4 * RU; x += NT) {
@@ -433,7 +454,7 @@ void dattn_fwd_kernel(FwdParams p) {
     }
   }
 
-  __syncthreads();  // saturation rows staged
+  __syncthreads();  // saturation rows and table window staged
 
   // a_i at both saturation ends: kr[row] . q_i with every A row equal
   float a_top = 0.f, a_bot = 0.f;
@@ -616,25 +637,37 @@ void dattn_fwd_kernel(FwdParams p) {
         if (p2c_mode == TERM_BAND) {
           // F[jh][v] = k_(j0+32kb+jh) . qr[T(vmin + v)], v over BM+31 distances
           const int vmin = (j0 + 32 * kb) - (i0 + BM - 1);
-          for (int vb = wave; vb < C::NBV; vb += NW) {
-            uint4 rf[NU];
-            load_half_row<NU>(rf, QRg + ((int64_t)rel_row(vmin + vb * 32 + li) * p.ld_rel + hoff +
-                                         lh * C::HALF) * ES);
-            const f32x16_t f = mma_chain<T, NU, NC>(kf, rf, f32x16_t{});
+          constexpr int FB = (C::NBV + NW - 1) / NW;   // F blocks of one wave
+          uint4 rf[FB][NU];
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-              Fw[(rr_of(r) + 4 * lh) * C::FWP + vb * 32 + li] = f[r];
+          for (int t = 0; t < FB; ++t) {
+            const int vb = wave + NW * t;
+            if (vb < C::NBV)
+              load_half_row<NU>(rf[t], QRg + ((int64_t)rel_row(vmin + vb * 32 + li) * p.ld_rel +
+                                              hoff + lh * C::HALF) * ES);
+          }
+#pragma unroll
+          for (int t = 0; t < FB; ++t) {
+            const int vb = wave + NW * t;
+            if (vb < C::NBV) {
+              const f32x16_t f = mma_chain<T, NU, NC>(kf, rf[t], f32x16_t{});
+#pragma unroll
+              for (int r = 0; r < 16; ++r)
+                Fw[(rr_of(r) + 4 * lh) * C::FWP + vb * 32 + li] = f[r];
+            }
           }
         }
         if (c2p_mode == TERM_BAND) {
           // E[u][i] = kr[T(umin + u)] . q_i, u over the wave's 63 distances
           const int umin = i0w - (j0 + 32 * kb + 31);
+          uint4 rf[2][NU];
+#pragma unroll
+          for (int ub = 0; ub < 2; ++ub)
+            load_half_row<NU>(rf[ub], KRg + ((int64_t)rel_row(umin + ub * 32 + li) * p.ld_rel + hoff +
+                                             lh * C::HALF) * ES);
 #pragma unroll
           for (int ub = 0; ub < 2; ++ub) {
-            uint4 rf[NU];
-            load_half_row<NU>(rf, KRg + ((int64_t)rel_row(umin + ub * 32 + li) * p.ld_rel + hoff +
-                                         lh * C::HALF) * ES);
-            const f32x16_t e = mma_chain<T, NU, NC>(rf, qf, f32x16_t{});
+            const f32x16_t e = mma_chain<T, NU, NC>(rf[ub], qf, f32x16_t{});
 #pragma unroll
             for (int r = 0; r < 16; ++r)
               Eww[(ub * 32 + rr_of(r) + 4 * lh) * 32 + li] = e[r];
