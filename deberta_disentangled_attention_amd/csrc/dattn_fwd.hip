@@ -81,6 +81,12 @@ template <> struct Ty<TBF16> {
   __device__ static __forceinline__ frag cvt8(f32x8_t x) {
     return __builtin_convertvector(x, bf16x8_t);
   }
+  // acc + the two bf16 halves of w
+  __device__ static __forceinline__ float sum2(uint32_t w, float acc) {
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, w),
+                                           __builtin_bit_cast(b2, 0x3f803f80u), acc, false);
+  }
 };
 
 template <> struct Ty<TF16> {
@@ -92,6 +98,12 @@ template <> struct Ty<TF16> {
   }
   __device__ static __forceinline__ frag cvt8(f32x8_t x) {
     return __builtin_convertvector(x, f16x8_t);
+  }
+  // acc + the two fp16 halves of w
+  __device__ static __forceinline__ float sum2(uint32_t w, float acc) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w), __builtin_bit_cast(h2, 0x3c003c00u), acc,
+                                  false);
   }
 };
 
@@ -154,6 +166,8 @@ struct Cfg {
   static_assert(K_BYTES % 16 == 0 && (OFF_E % 16) == 0 && (OFF_R % 16) == 0, "alignment");
   static_assert(BN % 32 == 0 && BN <= 64, "key tile");
   static_assert(UPR % 4 == 0 && UPR <= 32 && NT % UPR == 0, "staging groups");
+  static_assert(K_BYTES + V_BYTES + C_BYTES <= E_BYTES + F_BYTES, "second K/V buffer");
+  static_assert(V_BYTES % 16 == 0, "alignment");
 };
 
 // ----------------------------------------------------------------------------
@@ -523,9 +537,41 @@ void dattn_fwd_kernel(FwdParams p) {
       }
     }
   };
-  // cj_which >= 0: also write c_j = k_j . qr[row] (row: 0 top, 1 bottom) of
-  // the staged keys into cbuf
-  auto stage = [&](int cj_which) {
+  // fetch for tiles known to hold only valid keys: a uniform tile base plus
+  // per-thread byte offsets that do not change from tile to tile
+  uint32_t koff[C::JPT][2], voff[C::GPW][2];
+#pragma unroll
+  for (int s = 0; s < C::JPT; ++s) {
+    const int x = min(tid + s * NT, C::JOBS - 1);
+    const int pr = x / C::UPR, u = x % C::UPR;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      koff[s][h] = (uint32_t)(((2 * pr + h) * p.ld_k + hoff) * ES + 16 * u);
+  }
+#pragma unroll
+  for (int s = 0; s < C::GPW; ++s) {
+    int pr, u;
+    vjob_of(s, pr, u);
+    pr = min(pr, BN / 2 - 1);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      voff[s][h] = (uint32_t)(((2 * pr + h) * p.ld_v + hoff) * ES + 16 * u);
+  }
+  auto fetch_valid = [&](int j0) {
+    const unsigned char* kt = Kg + (base + j0) * p.ld_k * ES;
+    const unsigned char* vt = Vg + (base + j0) * p.ld_v * ES;
+#pragma unroll
+    for (int s = 0; s < C::JPT; ++s)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) pk[s][h] = ld16(kt + koff[s][h]);
+#pragma unroll
+    for (int s = 0; s < C::GPW; ++s)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) pv[s][h] = ld16(vt + voff[s][h]);
+  };
+  // stage into the given K / V^T / c_j buffers; cj_which >= 0: also write
+  // c_j = k_j . qr[row] (row: 0 top, 1 bottom) of the staged keys
+  auto stage = [&](unsigned char* Ks, unsigned char* Vt, float* cbuf, int cj_which) {
 #pragma unroll
     for (int s = 0; s < C::JPT; ++s) {
       const int x = tid + s * NT;
@@ -552,9 +598,10 @@ void dattn_fwd_kernel(FwdParams p) {
           uint32_t* vt = reinterpret_cast<uint32_t*>(Vt);
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const uint32_t lo = (e & 1) ? (a4[e >> 1] >> 16) : (a4[e >> 1] & 0xffffu);
-            const uint32_t hi = (e & 1) ? (b4[e >> 1] & 0xffff0000u) : (b4[e >> 1] << 16);
-            vt[((8 * u + e) * C::VPITCH + 2 * pr) >> 1] = lo | hi;
+            // bytes of the 16-bit element e of row 2pr (low) and of row 2pr+1 (high)
+            const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+            vt[((8 * u + e) * C::VPITCH + 2 * pr) >> 1] =
+                __builtin_amdgcn_perm(b4[e >> 1], a4[e >> 1], sel);
           }
         } else {
           uint2* vt = reinterpret_cast<uint2*>(Vt);
@@ -566,17 +613,176 @@ void dattn_fwd_kernel(FwdParams p) {
     }
   };
 
-  // per-lane V^T operand base: row dd = li of each 32-row block, keys from 4*lh
-  const unsigned char* v_base = Vt + (li * C::VPITCH + 4 * lh) * ES;
+  // per-lane V^T operand bases: row dd = li of each 32-row block, keys from 4*lh
+  const unsigned char* v_base0 = Vt + (li * C::VPITCH + 4 * lh) * ES;
   // per-lane gather bases (see the band writes below)
   const float* e_base = Eww + (li - 4 * lh + 4) * 32 + li;
   const float* f_base = Fw + 4 * lh * (C::FWP + 1) + (BM - 1 - 32 * wave - li);
+  // second K/V buffer of the far phase, in the band region (unused there)
+  unsigned char* Ks1 = smem + C::OFF_E;
+  unsigned char* Vt1 = Ks1 + C::K_BYTES;
+  float* cbuf1 = reinterpret_cast<float*>(Vt1 + C::V_BYTES);
+  const unsigned char* v_base1 = Vt1 + (li * C::VPITCH + 4 * lh) * ES;
 
-  fetch(0);
-  for (int j0 = 0; j0 < ext; j0 += BN) {
+  // accumulator input of the Q.K product: c_j of the constant P2C path
+  auto c_init = [&](const float* cb_base, int kb) -> f32x16_t {
+    const f32x4_t* cb = reinterpret_cast<const f32x4_t*>(cb_base + kb * 32 + 4 * lh);
+    const f32x4_t c0 = cb[0], c1 = cb[2], c2 = cb[4], c3 = cb[6];
+    const f32x8_t c01 = __builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7);
+    const f32x8_t c23 = __builtin_shufflevector(c2, c3, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_shufflevector(c01, c23, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+  };
+
+  // scores of a tile with no mask test and no band term: straight-line body
+  auto far_scores = [&](f32x16_t (&s)[C::NKB], const unsigned char* kbuf, const float* cb,
+                        auto p2c_const) {
+    constexpr bool PC = decltype(p2c_const)::value;
+    uint4 kf[C::NKB][NU];
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb)
+      lds_half_row<NU>(kf[kb], kbuf + ((kb * 32 + li) * C::KPITCH + lh * C::HALF) * ES);
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb) {
+      f32x16_t acc = f32x16_t{};
+      if constexpr (PC) acc = c_init(cb, kb);
+      s[kb] = mma_chain<T, NU, NC>(kf[kb], qf, acc);
+    }
+  };
+
+  // online softmax of a tile's scores and O^T += V^T P^T
+  auto softmax_pv = [&](f32x16_t (&s)[C::NKB], float a_off, const unsigned char* v_base) {
+    // P for the P.V MFMA, already rounded to the element type (16-bit types)
+    typename Ty<T>::frag pfrag[ES == 2 ? C::NKB : 1][2];
+    // ---- online softmax (base 2, scale folded) ---------------------------
+    // The exponent offset m_run is raised only when the tile maximum exceeds
+    // it by more than 8 (so every p <= 2^8), and the accumulators are then
+    // rescaled by alpha. O and l share the offset, so O / l does not depend
+    // on that choice; after the first tile the raise is rare, and the branch
+    // is laid out as the cold path. For 16-bit types the row sum is taken
+    // from the rounded P the P.V product uses (dot2 against (1, 1)).
+    {
+      const float tl2 = p.scale_log2;
+      const float off = a_off * tl2;
+      float mx4[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 4) {
+          mx4[0] = fmaxf(mx4[0], s[kb][r]);
+          mx4[1] = fmaxf(mx4[1], s[kb][r + 1]);
+          mx4[2] = fmaxf(mx4[2], s[kb][r + 2]);
+          mx4[3] = fmaxf(mx4[3], s[kb][r + 3]);
+        }
+      float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
+      mx = fmaxf(mx, wave_xor32(mx));
+      const float mt = (mx == NEG_INF) ? NEG_INF : fmaf(mx, tl2, off);
+      const bool raise = mt > m_run + 8.f;
+      if (__builtin_expect(__any(raise), 0)) {
+        const float m_new = raise ? mt : m_run;
+        // m_run == -inf: nothing accumulated yet, alpha = exp2(-inf) = 0
+        const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+        l_part *= alpha;
+#pragma unroll
+        for (int x = 0; x < C::NDB; ++x) o_acc[x] *= alpha;
+        m_run = m_new;
+      }
+      const float bias = off - (m_run == NEG_INF ? 0.f : m_run);
+      float ps4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+          f32x8_t e8;
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            e8[e] = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * c2 + e], tl2, bias));
+          if constexpr (ES == 2) {
+            pfrag[kb][c2] = Ty<T>::cvt8(e8);
+            const uint4 w = __builtin_bit_cast(uint4, pfrag[kb][c2]);
+            ps4[0] = Ty<T>::sum2(w.x, ps4[0]);
+            ps4[1] = Ty<T>::sum2(w.y, ps4[1]);
+            ps4[2] = Ty<T>::sum2(w.z, ps4[2]);
+            ps4[3] = Ty<T>::sum2(w.w, ps4[3]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              s[kb][8 * c2 + e] = e8[e];
+              ps4[e & 3] += e8[e];
+            }
+          }
+        }
+      l_part += (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
+    }
+
+    // ---- O^T += V^T P^T --------------------------------------------------
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb) {
+      if constexpr (ES == 2) {
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+          const typename Ty<T>::frag pb = pfrag[kb][c2];
+#pragma unroll
+          for (int db = 0; db < C::NDB; ++db) {
+            const unsigned char* vrow = v_base + (db * 32 * C::VPITCH + kb * 32 + 16 * c2) * ES;
+            const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+            const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
+            const typename Ty<T>::frag va = __builtin_bit_cast(
+                typename Ty<T>::frag, make_uint4(lo.x, lo.y, hi.x, hi.y));
+            o_acc[db] = Ty<T>::mma(va, pb, o_acc[db]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+#pragma unroll
+          for (int db = 0; db < C::NDB; ++db) {
+            const f32x4_t vv = *reinterpret_cast<const f32x4_t*>(
+                v_base + (db * 32 * C::VPITCH + kb * 32 + 8 * q4) * ES);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              o_acc[db] = Ty<T>::mma(vv[e], s[kb][4 * q4 + e], o_acc[db]);
+          }
+        }
+      }
+    }
+
+  };
+
+  // ---- tile classes -------------------------------------------------------
+  // Tiles before tm need no mask test. A tile is "far" when every pair of it
+  // lies beyond the saturation distances of each enabled term, on the side
+  // where keys precede the queries (tiles < FL) or follow them (FR <= t < tm).
+  // Other tiles ("general": [FL, FR) and [tm, ntiles)) run first, through
+  // the single-buffered path with band products; far tiles then reuse the
+  // band region of LDS as a second K/V buffer, one barrier per tile.
+  const int ntiles = (ext + BN - 1) / BN;
+  const int tm = key_end >= BN ? (key_end - BN) / BN + 1 : 0;
+  constexpr int BIG = 1 << 29;
+  const int lim_l = wg_qlo - BN + 1 + min(has_p2c ? sat_bot : BIG, has_c2p ? -sat_top : BIG);
+  const int lim_r = wg_qhi + max(has_p2c ? sat_top : -BIG, has_c2p ? -sat_bot : -BIG);
+  const int FL = lim_l >= 0 ? min(lim_l / BN + 1, tm) : 0;
+  const int FR = min(max(lim_r > 0 ? (lim_r + BN - 1) / BN : 0, FL), tm);
+  auto next_general = [&](int t) {
+    int n = t + 1;
+    if (n >= FR && n < tm) n = tm;
+    return n < ntiles ? n : -1;
+  };
+  auto next_far = [&](int t) {
+    int n = t + 1;
+    if (n >= FL && n < FR) n = FR;
+    return n < tm ? n : -1;
+  };
+  const int first_general = FL < FR ? FL : (tm < ntiles ? tm : -1);
+  const int first_far = FL > 0 ? 0 : (FR < tm ? FR : -1);
+
+  // ---- phase 1: general tiles (band products, masks) ------------------------
+  if (first_general >= 0) fetch(first_general * BN);
+  else if (first_far >= 0) fetch(first_far * BN);
+  for (int t = first_general; t >= 0; t = next_general(t)) {
+    const int j0 = t * BN;
     const bool need_mask = j0 + BN > key_end;
 
-    // ---- path of each position term for this tile -----------------------
+    // path of each position term for this tile
     const int k_lo = j0, k_hi = min(j0 + BN, ext) - 1;
     int p2c_mode = TERM_OFF, p2c_which = 0;   // which: 0 top row, 1 bottom row
     if (has_p2c) {
@@ -592,42 +798,19 @@ void dattn_fwd_kernel(FwdParams p) {
       else c2p_mode = TERM_BAND;
     }
 
-    stage(p2c_mode == TERM_CONST ? p2c_which : -1);
-    if (j0 + BN < ext) fetch(j0 + BN);
+    stage(Ks, Vt, cbuf, p2c_mode == TERM_CONST ? p2c_which : -1);
+    {
+      const int tn = next_general(t);
+      if (tn >= 0) fetch(tn * BN);
+      else if (first_far >= 0) fetch(first_far * BN);   // the far phase's first tile
+    }
     __syncthreads();  // K, V^T (and c_j) of this tile staged
 
-    // A tile that needs no mask test and takes the constant path (or no
-    // path) for both position terms runs a straight-line body.
-    const bool far_tile = !need_mask && c2p_mode != TERM_BAND && p2c_mode != TERM_BAND;
-
-    // accumulator input of the Q.K product: c_j of the constant P2C path
-    auto c_init = [&](int kb) -> f32x16_t {
-      const f32x4_t* cb = reinterpret_cast<const f32x4_t*>(cbuf + kb * 32 + 4 * lh);
-      const f32x4_t c0 = cb[0], c1 = cb[2], c2 = cb[4], c3 = cb[6];
-      const f32x8_t c01 = __builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7);
-      const f32x8_t c23 = __builtin_shufflevector(c2, c3, 0, 1, 2, 3, 4, 5, 6, 7);
-      return __builtin_shufflevector(c01, c23, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
-    };
-
-    // ---- scores -------------------------------------------------------
     f32x16_t s[C::NKB];
-    auto far_scores = [&](auto p2c_const) {
-      constexpr bool PC = decltype(p2c_const)::value;
-      uint4 kf[C::NKB][NU];
-#pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb)
-        lds_half_row<NU>(kf[kb], Ks + ((kb * 32 + li) * C::KPITCH + lh * C::HALF) * ES);
-#pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb) {
-        f32x16_t acc = f32x16_t{};
-        if constexpr (PC) acc = c_init(kb);
-        s[kb] = mma_chain<T, NU, NC>(kf[kb], qf, acc);
-      }
-    };
-
+    const bool far_tile = !need_mask && c2p_mode != TERM_BAND && p2c_mode != TERM_BAND;
     if (far_tile) {
-      if (p2c_mode == TERM_CONST) far_scores(std::true_type{});
-      else far_scores(std::false_type{});
+      if (p2c_mode == TERM_CONST) far_scores(s, Ks, cbuf, std::true_type{});
+      else far_scores(s, Ks, cbuf, std::false_type{});
     } else {
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb) {
@@ -675,7 +858,7 @@ void dattn_fwd_kernel(FwdParams p) {
         }
         if (p2c_mode == TERM_BAND) __syncthreads();  // F complete
 
-        f32x16_t acc = (p2c_mode == TERM_CONST) ? c_init(kb) : f32x16_t{};
+        f32x16_t acc = (p2c_mode == TERM_CONST) ? c_init(cbuf, kb) : f32x16_t{};
         acc = mma_chain<T, NU, NC>(kf, qf, acc);
         if (c2p_mode == TERM_BAND) {
 #pragma unroll
@@ -698,96 +881,39 @@ void dattn_fwd_kernel(FwdParams p) {
         if (p2c_mode == TERM_BAND && kb + 1 < C::NKB) __syncthreads();  // F reused
       }
     }
-
-    // P for the P.V MFMA, already rounded to the element type (16-bit types)
-    typename Ty<T>::frag pfrag[ES == 2 ? C::NKB : 1][2];
-    // ---- online softmax (base 2, scale folded) ---------------------------
-    // The exponent offset m_run is raised only when the tile maximum exceeds
-    // it by more than 8 (so every p <= 2^8), and the accumulators are then
-    // rescaled by alpha. O and l share the offset, so O / l does not depend
-    // on that choice; after the first tile alpha is almost always exactly 1.
-    // The multiply is unconditional: a branch around it makes the register
-    // allocator move the O accumulators every tile, which costs more.
-    {
-      const float tl2 = p.scale_log2;
-      const float off = a_off * tl2;
-      float mx4[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
-#pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; r += 4) {
-          mx4[0] = fmaxf(mx4[0], s[kb][r]);
-          mx4[1] = fmaxf(mx4[1], s[kb][r + 1]);
-          mx4[2] = fmaxf(mx4[2], s[kb][r + 2]);
-          mx4[3] = fmaxf(mx4[3], s[kb][r + 3]);
-        }
-      float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
-      mx = fmaxf(mx, wave_xor32(mx));
-      const float mt = (mx == NEG_INF) ? NEG_INF : fmaf(mx, tl2, off);
-      const bool raise = mt > m_run + 8.f;
-      {
-        const float m_new = raise ? mt : m_run;
-        const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
-        l_part *= alpha;
-#pragma unroll
-        for (int x = 0; x < C::NDB; ++x) o_acc[x] *= alpha;
-        m_run = m_new;
-      }
-      const float bias = off - (m_run == NEG_INF ? 0.f : m_run);
-      float ps4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-          f32x8_t e8;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float x = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * c2 + e], tl2, bias));
-            e8[e] = x;
-            ps4[e & 3] += x;
-          }
-          if constexpr (ES == 2) pfrag[kb][c2] = Ty<T>::cvt8(e8);
-          else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) s[kb][8 * c2 + e] = e8[e];
-          }
-        }
-      l_part += (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
-    }
-
-    // ---- O^T += V^T P^T --------------------------------------------------
-#pragma unroll
-    for (int kb = 0; kb < C::NKB; ++kb) {
-      if constexpr (ES == 2) {
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-          const typename Ty<T>::frag pb = pfrag[kb][c2];
-#pragma unroll
-          for (int db = 0; db < C::NDB; ++db) {
-            const unsigned char* vrow = v_base + (db * 32 * C::VPITCH + kb * 32 + 16 * c2) * ES;
-            const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-            const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
-            const typename Ty<T>::frag va = __builtin_bit_cast(
-                typename Ty<T>::frag, make_uint4(lo.x, lo.y, hi.x, hi.y));
-            o_acc[db] = Ty<T>::mma(va, pb, o_acc[db]);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-#pragma unroll
-          for (int db = 0; db < C::NDB; ++db) {
-            const f32x4_t vv = *reinterpret_cast<const f32x4_t*>(
-                v_base + (db * 32 * C::VPITCH + kb * 32 + 8 * q4) * ES);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              o_acc[db] = Ty<T>::mma(vv[e], s[kb][4 * q4 + e], o_acc[db]);
-          }
-        }
-      }
-    }
-
+    softmax_pv(s, a_off, v_base0);
     __syncthreads();  // tile buffers free for the next key tile
+  }
+
+  // ---- phase 2: far tiles, double-buffered ----------------------------------
+  if (first_far >= 0) {
+    // which qr row the constant P2C term reads, and the C2P offset, per side
+    auto p2c_row_of = [&](int t) { return has_p2c ? (t < FL ? 1 : 0) : -1; };
+    int t = first_far;
+    stage(Ks, Vt, cbuf, p2c_row_of(t));
+    int tn = next_far(t);
+    if (tn >= 0) fetch(tn * BN);
+    __syncthreads();
+    int b = 0;
+    while (t >= 0) {
+      const int tnn = tn >= 0 ? next_far(tn) : -1;
+      if (tn >= 0) {
+        // the other buffer was last read by the previous tile, which every
+        // wave has finished (barrier at the end of the previous iteration)
+        if (b) stage(Ks, Vt, cbuf, p2c_row_of(tn));
+        else stage(Ks1, Vt1, cbuf1, p2c_row_of(tn));
+        if (tnn >= 0) fetch(tnn * BN);
+      }
+      const float a_off = has_c2p ? (t < FL ? a_top : a_bot) : 0.f;
+      f32x16_t s[C::NKB];
+      if (has_p2c) far_scores(s, b ? Ks1 : Ks, b ? cbuf1 : cbuf, std::true_type{});
+      else far_scores(s, b ? Ks1 : Ks, b ? cbuf1 : cbuf, std::false_type{});
+      softmax_pv(s, a_off, b ? v_base1 : v_base0);
+      __syncthreads();  // next tile staged; this tile's buffer free
+      t = tn;
+      tn = tnn;
+      b ^= 1;
+    }
   }
 
   // ---- epilogue: normalise, zero padded rows, store ----------------------
