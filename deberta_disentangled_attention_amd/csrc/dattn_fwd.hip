@@ -200,6 +200,25 @@ __device__ __forceinline__ f32x16_t mma_chain(const uint4 (&a)[NU], const uint4 
   return acc;
 }
 
+// acc += A . B^T where A's half-row fragment is read from LDS a few units at
+// a time (keeps few registers live for wide fp32 rows)
+template <class T, int NU, int NC>
+__device__ __forceinline__ f32x16_t mma_chain_lds(const unsigned char* a_lds, const uint4 (&b)[NU],
+                                                  f32x16_t acc) {
+  constexpr int CPU = NC / NU;   // MFMAs per 16-byte unit
+#pragma unroll
+  for (int x = 0; x < NU; ++x) {
+    const uint4 a = *reinterpret_cast<const uint4*>(a_lds + 16 * x);
+#pragma unroll
+    for (int c = 0; c < CPU; ++c) {
+      uint4 one[1] = {a};
+      uint4 bb[1] = {b[x]};
+      acc = Ty<T>::mma(frag_at<T, 1>(one, c), frag_at<T, 1>(bb, c), acc);
+    }
+  }
+  return acc;
+}
+
 template <int NU>
 __device__ __forceinline__ void load_half_row(uint4 (&u)[NU], const unsigned char* p) {
 #pragma unroll
@@ -637,15 +656,25 @@ void dattn_fwd_kernel(FwdParams p) {
   auto far_scores = [&](f32x16_t (&s)[C::NKB], const unsigned char* kbuf, const float* cb,
                         auto p2c_const) {
     constexpr bool PC = decltype(p2c_const)::value;
-    uint4 kf[C::NKB][NU];
+    if constexpr (ES == 4) {
 #pragma unroll
-    for (int kb = 0; kb < C::NKB; ++kb)
-      lds_half_row<NU>(kf[kb], kbuf + ((kb * 32 + li) * C::KPITCH + lh * C::HALF) * ES);
+      for (int kb = 0; kb < C::NKB; ++kb) {
+        f32x16_t acc = f32x16_t{};
+        if constexpr (PC) acc = c_init(cb, kb);
+        s[kb] = mma_chain_lds<T, NU, NC>(kbuf + ((kb * 32 + li) * C::KPITCH + lh * C::HALF) * ES, qf,
+                                         acc);
+      }
+    } else {
+      uint4 kf[C::NKB][NU];
 #pragma unroll
-    for (int kb = 0; kb < C::NKB; ++kb) {
-      f32x16_t acc = f32x16_t{};
-      if constexpr (PC) acc = c_init(cb, kb);
-      s[kb] = mma_chain<T, NU, NC>(kf[kb], qf, acc);
+      for (int kb = 0; kb < C::NKB; ++kb)
+        lds_half_row<NU>(kf[kb], kbuf + ((kb * 32 + li) * C::KPITCH + lh * C::HALF) * ES);
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb) {
+        f32x16_t acc = f32x16_t{};
+        if constexpr (PC) acc = c_init(cb, kb);
+        s[kb] = mma_chain<T, NU, NC>(kf[kb], qf, acc);
+      }
     }
   };
 
@@ -814,52 +843,68 @@ void dattn_fwd_kernel(FwdParams p) {
     } else {
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb) {
-        uint4 kf[NU];
-        lds_half_row<NU>(kf, Ks + ((kb * 32 + li) * C::KPITCH + lh * C::HALF) * ES);
+        // fp32 rows are wide: K is then read from LDS per MFMA instead of
+        // held in registers, and relative rows are fetched one block at a time
+        constexpr bool WIDE = (ES == 4);
+        const unsigned char* k_lds = Ks + ((kb * 32 + li) * C::KPITCH + lh * C::HALF) * ES;
+        uint4 kf[WIDE ? 1 : NU];
+        if constexpr (!WIDE) lds_half_row<NU>(kf, k_lds);
+        auto kchain = [&](const uint4 (&b)[NU], f32x16_t acc) {
+          if constexpr (WIDE) return mma_chain_lds<T, NU, NC>(k_lds, b, acc);
+          else return mma_chain<T, NU, NC>(kf, b, acc);
+        };
 
         if (p2c_mode == TERM_BAND) {
           // F[jh][v] = k_(j0+32kb+jh) . qr[T(vmin + v)], v over BM+31 distances
           const int vmin = (j0 + 32 * kb) - (i0 + BM - 1);
           constexpr int FB = (C::NBV + NW - 1) / NW;   // F blocks of one wave
-          uint4 rf[FB][NU];
+          constexpr int FL = WIDE ? 1 : FB;             // blocks loaded together
 #pragma unroll
-          for (int t = 0; t < FB; ++t) {
-            const int vb = wave + NW * t;
-            if (vb < C::NBV)
-              load_half_row<NU>(rf[t], QRg + ((int64_t)rel_row(vmin + vb * 32 + li) * p.ld_rel +
-                                              hoff + lh * C::HALF) * ES);
-          }
+          for (int t0 = 0; t0 < FB; t0 += FL) {
+            uint4 rf[FL][NU];
 #pragma unroll
-          for (int t = 0; t < FB; ++t) {
-            const int vb = wave + NW * t;
-            if (vb < C::NBV) {
-              const f32x16_t f = mma_chain<T, NU, NC>(kf, rf[t], f32x16_t{});
+            for (int t = 0; t < FL; ++t) {
+              const int vb = wave + NW * (t0 + t);
+              if (vb < C::NBV)
+                load_half_row<NU>(rf[t], QRg + ((int64_t)rel_row(vmin + vb * 32 + li) * p.ld_rel +
+                                                hoff + lh * C::HALF) * ES);
+            }
 #pragma unroll
-              for (int r = 0; r < 16; ++r)
-                Fw[(rr_of(r) + 4 * lh) * C::FWP + vb * 32 + li] = f[r];
+            for (int t = 0; t < FL; ++t) {
+              const int vb = wave + NW * (t0 + t);
+              if (vb < C::NBV) {
+                const f32x16_t f = kchain(rf[t], f32x16_t{});
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                  Fw[(rr_of(r) + 4 * lh) * C::FWP + vb * 32 + li] = f[r];
+              }
             }
           }
         }
         if (c2p_mode == TERM_BAND) {
           // E[u][i] = kr[T(umin + u)] . q_i, u over the wave's 63 distances
           const int umin = i0w - (j0 + 32 * kb + 31);
-          uint4 rf[2][NU];
+          constexpr int EL = WIDE ? 1 : 2;              // blocks loaded together
 #pragma unroll
-          for (int ub = 0; ub < 2; ++ub)
-            load_half_row<NU>(rf[ub], KRg + ((int64_t)rel_row(umin + ub * 32 + li) * p.ld_rel + hoff +
-                                             lh * C::HALF) * ES);
+          for (int u0 = 0; u0 < 2; u0 += EL) {
+            uint4 rf[EL][NU];
 #pragma unroll
-          for (int ub = 0; ub < 2; ++ub) {
-            const f32x16_t e = mma_chain<T, NU, NC>(rf[ub], qf, f32x16_t{});
+            for (int ub = 0; ub < EL; ++ub)
+              load_half_row<NU>(rf[ub], KRg + ((int64_t)rel_row(umin + (u0 + ub) * 32 + li) *
+                                                   p.ld_rel + hoff + lh * C::HALF) * ES);
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-              Eww[(ub * 32 + rr_of(r) + 4 * lh) * 32 + li] = e[r];
+            for (int ub = 0; ub < EL; ++ub) {
+              const f32x16_t e = mma_chain<T, NU, NC>(rf[ub], qf, f32x16_t{});
+#pragma unroll
+              for (int r = 0; r < 16; ++r)
+                Eww[((u0 + ub) * 32 + rr_of(r) + 4 * lh) * 32 + li] = e[r];
+            }
           }
         }
         if (p2c_mode == TERM_BAND) __syncthreads();  // F complete
 
         f32x16_t acc = (p2c_mode == TERM_CONST) ? c_init(cbuf, kb) : f32x16_t{};
-        acc = mma_chain<T, NU, NC>(kf, qf, acc);
+        acc = kchain(qf, acc);
         if (c2p_mode == TERM_BAND) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[r] += e_base[(27 - rr_of(r)) * 32];
