@@ -78,6 +78,9 @@ template <> struct Ty<TBF16> {
   __device__ static __forceinline__ f32x16_t mma(frag a, frag b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
+  __device__ static __forceinline__ f32x4_t mma16(frag a, frag b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
   __device__ static __forceinline__ frag cvt8(f32x8_t x) {
     return __builtin_convertvector(x, bf16x8_t);
   }
@@ -95,6 +98,9 @@ template <> struct Ty<TF16> {
   typedef f16x8_t frag;
   __device__ static __forceinline__ f32x16_t mma(frag a, frag b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ f32x4_t mma16(frag a, frag b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
   }
   __device__ static __forceinline__ frag cvt8(f32x8_t x) {
     return __builtin_convertvector(x, f16x8_t);
@@ -130,18 +136,22 @@ struct Cfg {
   static constexpr int NC = HALF / Ty<T>::LANE_K;    // MFMAs per d-long product
   static constexpr int NBV = NW + 1;                 // F blocks per 32-key half (BM+31 distances)
   static constexpr int KPITCH = D + EPU;             // K tile row pitch (elements)
-  // V^T row pitch (elements): BN+4 keeps the P.V operand reads (8 bytes per
-  // lane for 16-bit types, 16 for fp32) aligned and, with the staging order
-  // below, both the reads and the transposing stores free of bank conflicts.
-  static constexpr int VPITCH = BN + 4;
+  // V^T row pitch (elements). 16-bit types: BN+8, so every P.V operand is
+  // one aligned 16-byte read and rows 8 apart fall 32 banks apart; fp32:
+  // BN+4 (16-byte reads). With the staging order below both the reads and
+  // the transposing stores are free of bank conflicts.
+  static constexpr int VPITCH = ES == 2 ? BN + 8 : BN + 4;
   static constexpr int EW = 64 * 32;                 // floats of E per wave (64 distances x 32 queries)
   static constexpr int FWP = 32 * NBV;               // F row pitch (floats)
   static constexpr int UPR = D * ES / 16;            // 16-byte units per K/V row
   static constexpr int JOBS = (BN / 2) * UPR;        // staging jobs: (row pair, unit)
   static constexpr int JPT = (JOBS + NT - 1) / NT;   // jobs per thread
-  // V staging: a wave moves 16 row pairs x 4 units per step (one group)
-  static constexpr int UG = UPR / 4;                 // unit groups per row
-  static constexpr int GROUPS = UG * (BN / 32);      // groups per tile
+  // V staging: a wave moves one group per step, 16-bit types 32 row pairs x
+  // 2 units, fp32 16 row pairs x 4 units
+  static constexpr int VG_U = ES == 2 ? 2 : 4;       // units per group
+  static constexpr int VG_P = 64 / VG_U;             // row pairs per group
+  static constexpr int UG = UPR / VG_U;              // unit groups per row
+  static constexpr int GROUPS = UG * (BN / 2 / VG_P); // groups per tile
   static constexpr int GPW = (GROUPS + NW - 1) / NW; // groups per wave
   static constexpr int K_BYTES = BN * KPITCH * ES;
   static constexpr int V_BYTES = (D * VPITCH * ES + 15) / 16 * 16;
@@ -154,8 +164,17 @@ struct Cfg {
   static constexpr int OFF_V = K_BYTES;
   static constexpr int OFF_E = OFF_V + V_BYTES;
   static constexpr int OFF_F = OFF_E + E_BYTES;
-  static constexpr int OFF_C = OFF_F + F_BYTES;
-  static constexpr int OFF_R = OFF_C + C_BYTES;
+  // far-tile ring (16-bit types): NSTAGE slots of a K tile and a V tile, both
+  // dense [BN][D] rows written by direct-to-LDS loads; it reuses the region
+  // of the general-tile buffers above
+  static constexpr int NSTAGE = 4;
+  static constexpr int KT_BYTES = BN * UPR * 16;
+  static constexpr int SLOT_BYTES = 2 * KT_BYTES;
+  static constexpr int RING_BYTES = ES == 2 ? NSTAGE * SLOT_BYTES : 0;
+  static constexpr int P1_BYTES = OFF_F + F_BYTES;
+  static constexpr int OFF_C = P1_BYTES > RING_BYTES ? P1_BYTES : RING_BYTES;
+  static constexpr int OFF_CR = OFF_C + C_BYTES;     // c_j of two ring tiles
+  static constexpr int OFF_R = OFF_CR + 2 * C_BYTES;
   static constexpr int OFF_TW = OFF_R + R_BYTES;
   static constexpr int OFF_MISC = OFF_TW + TW_BYTES;
   static constexpr int LDS_BYTES = OFF_MISC + 64;
@@ -166,7 +185,19 @@ struct Cfg {
   static_assert(K_BYTES % 16 == 0 && (OFF_E % 16) == 0 && (OFF_R % 16) == 0, "alignment");
   static_assert(BN % 32 == 0 && BN <= 64, "key tile");
   static_assert(UPR % 4 == 0 && UPR <= 32 && NT % UPR == 0, "staging groups");
+  static_assert((BN / 2) % VG_P == 0, "V staging groups");
   static_assert(K_BYTES + V_BYTES + C_BYTES <= E_BYTES + F_BYTES, "second K/V buffer");
+  static_assert(ES == 4 || (UPR >= 4 && UPR <= 16 && UPR % NW == 0 && BN == 64), "ring loads");
+  // direct-to-LDS loads: one wave instruction moves 64 units (1 KB) of a tile
+  static constexpr int DMA_PER_TILE = BN * UPR / 64;          // per K (and per V) tile
+  static constexpr int DMA_PER_WAVE = DMA_PER_TILE / NW;      // per K (and per V) tile
+  // XOR swizzles of the 16-byte units of ring rows. K: the 16 rows read by
+  // one quarter-wave of an MFMA operand load land in distinct bank groups.
+  // V: the four keys x 32 bytes of a quarter-wave transposing read do.
+  __device__ static constexpr int swz_k(int r) { return (r * UPR / 16) % UPR; }
+  __device__ static constexpr int swz_v(int r) {
+    return UPR == 8 ? ((r >> 1) & 1) << 2 : (UPR == 16 ? (r & 3) << 2 : 0);
+  }
   static_assert(V_BYTES % 16 == 0, "alignment");
 };
 
@@ -233,10 +264,40 @@ __device__ __forceinline__ void lds_half_row(uint4 (&u)[NU], const unsigned char
 
 __device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32); }
 
+// Direct-to-LDS load (global_load_lds_dwordx4): lane i's 16 bytes at
+// gbase + voff are written to LDS byte address lds + 16 i. The data bypasses
+// the registers; completion is tracked by this wave's vmcnt.
+__device__ __forceinline__ void dma16(uint32_t lds, const void* gbase, uint32_t voff) {
+  const uint64_t g = (uint64_t)(size_t)gbase;
+  const uint64_t gu = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(g >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)g);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(gu) : "memory", "m0");
+}
+
+// wait until at most N of this wave's vector-memory operations are in flight
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
+}
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+// Transposing LDS read (ds_read_b64_tr_b16). In each group of 16 lanes, lane
+// t names a 4-element chunk X_t; lane t receives X_(t/4 + 4e)[t % 4], e = 0..3.
+__device__ __forceinline__ uint2 lds_tr16(const unsigned char* p) {
+  const s16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4_t*)(p));
+  return __builtin_bit_cast(uint2, r);
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL,
-                                                             0xf, 0xf, false));
+  // every lane has a source lane in the patterns used here; bound_ctrl lets
+  // the move fuse into the consuming add
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                                                0xf, 0xf, true));
 }
 
 // sum over each aligned group of N consecutive lanes (N = 4, 8, 16 or 32);
@@ -275,6 +336,15 @@ __device__ __forceinline__ float dot16(uint4 a, uint4 b) {
 
 // key offset (within a 32-key block) of accumulator register r in lane half 0
 __device__ __forceinline__ constexpr int rr_of(int r) { return 8 * (r >> 2) + (r & 3); }
+
+// Column of key k in a 16-bit V^T tile row. The P.V MFMA takes, in lane half
+// h, the eight P values of registers 8c..8c+7 as its reduction elements
+// 8h..8h+7; those are keys {16c + 4h + 0..3, 16c + 8 + 4h + 0..3}. Storing each
+// group of 16 keys in the order 0-3, 8-11, 4-7, 12-15 (bits 2 and 3 of the
+// key swapped) makes the matching eight V^T elements contiguous.
+__device__ __forceinline__ constexpr int v_pos(int k) {
+  return (k & ~15) | (k & 3) | ((k & 4) << 1) | ((k & 8) >> 1);
+}
 
 // Smallest x in [0, n) with pred(x) true (pred monotone false -> true), or n.
 // Every thread of the workgroup must call it; NT-way parallel search.
@@ -326,6 +396,7 @@ void dattn_fwd_kernel(FwdParams p) {
   float* Ew = reinterpret_cast<float*>(smem + C::OFF_E);
   float* Fw = reinterpret_cast<float*>(smem + C::OFF_F);
   float* cbuf = reinterpret_cast<float*>(smem + C::OFF_C);
+  float* cring = reinterpret_cast<float*>(smem + C::OFF_CR);
   unsigned char* Rrows = smem + C::OFF_R;   // qr_top, qr_bot, kr_top, kr_bot
   int* misc = reinterpret_cast<int*>(smem + C::OFF_MISC);
   int* Tw = reinterpret_cast<int*>(smem + C::OFF_TW);   // table rows for sat_bot < d < sat_top
@@ -521,8 +592,8 @@ void dattn_fwd_kernel(FwdParams p) {
   auto vjob_of = [&](int s, int& pr, int& u) -> bool {
     const int g = wave + NW * s;
     const int ug = g % C::UG, pg = g / C::UG;
-    u = 4 * ug + (lane >> 4);
-    pr = 16 * pg + (lane & 15);
+    u = C::VG_U * ug + lane / C::VG_P;
+    pr = C::VG_P * pg + lane % C::VG_P;
     return g < C::GROUPS;
   };
   auto key_ok = [&](int j, bool nm) {
@@ -576,7 +647,7 @@ void dattn_fwd_kernel(FwdParams p) {
     for (int h = 0; h < 2; ++h)
       voff[s][h] = (uint32_t)(((2 * pr + h) * p.ld_v + hoff) * ES + 16 * u);
   }
-  auto fetch_valid = [&](int j0) {
+  auto fetch_valid = [&](int j0) {   // requires j0 + BN <= key_end
     const unsigned char* kt = Kg + (base + j0) * p.ld_k * ES;
     const unsigned char* vt = Vg + (base + j0) * p.ld_v * ES;
 #pragma unroll
@@ -613,13 +684,15 @@ void dattn_fwd_kernel(FwdParams p) {
         const uint32_t a4[4] = {pv[s][0].x, pv[s][0].y, pv[s][0].z, pv[s][0].w};
         const uint32_t b4[4] = {pv[s][1].x, pv[s][1].y, pv[s][1].z, pv[s][1].w};
         if constexpr (ES == 2) {
-          // element e of both rows -> one dword of V^T row (8u + e)
+          // element e of both rows -> one dword of V^T row (8u + e), at the
+          // pair's position in the operand order (see v_pos)
           uint32_t* vt = reinterpret_cast<uint32_t*>(Vt);
+          const int pp = v_pos(2 * pr) >> 1;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             // bytes of the 16-bit element e of row 2pr (low) and of row 2pr+1 (high)
             const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-            vt[((8 * u + e) * C::VPITCH + 2 * pr) >> 1] =
+            vt[(((8 * u + e) * C::VPITCH) >> 1) + pp] =
                 __builtin_amdgcn_perm(b4[e >> 1], a4[e >> 1], sel);
           }
         } else {
@@ -632,8 +705,10 @@ void dattn_fwd_kernel(FwdParams p) {
     }
   };
 
-  // per-lane V^T operand bases: row dd = li of each 32-row block, keys from 4*lh
-  const unsigned char* v_base0 = Vt + (li * C::VPITCH + 4 * lh) * ES;
+  // per-lane V^T operand bases: row dd = li of each 32-row block; 16-bit types
+  // read columns 8*lh.. of each 16-key group, fp32 keys 4*lh..
+  constexpr int V_LANE = ES == 2 ? 8 : 4;
+  const unsigned char* v_base0 = Vt + (li * C::VPITCH + V_LANE * lh) * ES;
   // per-lane gather bases (see the band writes below)
   const float* e_base = Eww + (li - 4 * lh + 4) * 32 + li;
   const float* f_base = Fw + 4 * lh * (C::FWP + 1) + (BM - 1 - 32 * wave - li);
@@ -641,7 +716,18 @@ void dattn_fwd_kernel(FwdParams p) {
   unsigned char* Ks1 = smem + C::OFF_E;
   unsigned char* Vt1 = Ks1 + C::K_BYTES;
   float* cbuf1 = reinterpret_cast<float*>(Vt1 + C::V_BYTES);
-  const unsigned char* v_base1 = Vt1 + (li * C::VPITCH + 4 * lh) * ES;
+  const unsigned char* v_base1 = Vt1 + (li * C::VPITCH + V_LANE * lh) * ES;
+
+  // V^T operands from a staged (transposed) V tile
+  auto vop_staged = [&](const unsigned char* v_base) {
+    return [=](int kb, int c, int db) {
+      if constexpr (ES == 2)
+        return __builtin_bit_cast(typename Ty<T>::frag,
+                                  ld16(v_base + (db * 32 * C::VPITCH + kb * 32 + 16 * c) * ES));
+      else
+        return *reinterpret_cast<const f32x4_t*>(v_base + (db * 32 * C::VPITCH + kb * 32 + 8 * c) * ES);
+    };
+  };
 
   // accumulator input of the Q.K product: c_j of the constant P2C path
   auto c_init = [&](const float* cb_base, int kb) -> f32x16_t {
@@ -679,7 +765,9 @@ void dattn_fwd_kernel(FwdParams p) {
   };
 
   // online softmax of a tile's scores and O^T += V^T P^T
-  auto softmax_pv = [&](f32x16_t (&s)[C::NKB], float a_off, const unsigned char* v_base) {
+  // vop(kb, c, db): V^T operand of the P.V MFMA for key block kb, 16-key
+  // group c (16-bit types) or 8-key group c (fp32), head-dim block db
+  auto softmax_pv = [&](f32x16_t (&s)[C::NKB], float a_off, auto vop) {
     // P for the P.V MFMA, already rounded to the element type (16-bit types)
     typename Ty<T>::frag pfrag[ES == 2 ? C::NKB : 1][2];
     // ---- online softmax (base 2, scale folded) ---------------------------
@@ -702,11 +790,15 @@ void dattn_fwd_kernel(FwdParams p) {
           mx4[2] = fmaxf(mx4[2], s[kb][r + 2]);
           mx4[3] = fmaxf(mx4[3], s[kb][r + 3]);
         }
-      float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
-      mx = fmaxf(mx, wave_xor32(mx));
-      const float mt = (mx == NEG_INF) ? NEG_INF : fmaf(mx, tl2, off);
-      const bool raise = mt > m_run + 8.f;
-      if (__builtin_expect(__any(raise), 0)) {
+      // This lane's half of the row decides alone whether a raise may be
+      // needed; only then is the maximum of both halves formed, so the two
+      // lanes of a query always move m_run together.
+      const float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
+      const float mt_half = (mx == NEG_INF) ? NEG_INF : fmaf(mx, tl2, off);
+      if (__builtin_expect(__any(mt_half > m_run + 8.f), 0)) {
+        const float mxf = fmaxf(mx, wave_xor32(mx));
+        const float mt = (mxf == NEG_INF) ? NEG_INF : fmaf(mxf, tl2, off);
+        const bool raise = mt > m_run + 8.f;
         const float m_new = raise ? mt : m_run;
         // m_run == -inf: nothing accumulated yet, alpha = exp2(-inf) = 0
         const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
@@ -752,12 +844,7 @@ void dattn_fwd_kernel(FwdParams p) {
           const typename Ty<T>::frag pb = pfrag[kb][c2];
 #pragma unroll
           for (int db = 0; db < C::NDB; ++db) {
-            const unsigned char* vrow = v_base + (db * 32 * C::VPITCH + kb * 32 + 16 * c2) * ES;
-            const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-            const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
-            const typename Ty<T>::frag va = __builtin_bit_cast(
-                typename Ty<T>::frag, make_uint4(lo.x, lo.y, hi.x, hi.y));
-            o_acc[db] = Ty<T>::mma(va, pb, o_acc[db]);
+            o_acc[db] = Ty<T>::mma(vop(kb, c2, db), pb, o_acc[db]);
           }
         }
       } else {
@@ -765,8 +852,7 @@ void dattn_fwd_kernel(FwdParams p) {
         for (int q4 = 0; q4 < 4; ++q4) {
 #pragma unroll
           for (int db = 0; db < C::NDB; ++db) {
-            const f32x4_t vv = *reinterpret_cast<const f32x4_t*>(
-                v_base + (db * 32 * C::VPITCH + kb * 32 + 8 * q4) * ES);
+            const f32x4_t vv = vop(kb, q4, db);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
               o_acc[db] = Ty<T>::mma(vv[e], s[kb][4 * q4 + e], o_acc[db]);
@@ -806,7 +892,7 @@ void dattn_fwd_kernel(FwdParams p) {
 
   // ---- phase 1: general tiles (band products, masks) ------------------------
   if (first_general >= 0) fetch(first_general * BN);
-  else if (first_far >= 0) fetch(first_far * BN);
+  else if (ES == 4 && first_far >= 0) fetch(first_far * BN);
   for (int t = first_general; t >= 0; t = next_general(t)) {
     const int j0 = t * BN;
     const bool need_mask = j0 + BN > key_end;
@@ -830,8 +916,12 @@ void dattn_fwd_kernel(FwdParams p) {
     stage(Ks, Vt, cbuf, p2c_mode == TERM_CONST ? p2c_which : -1);
     {
       const int tn = next_general(t);
-      if (tn >= 0) fetch(tn * BN);
-      else if (first_far >= 0) fetch(first_far * BN);   // the far phase's first tile
+      if (tn >= 0) {
+        if (tn < tm) fetch_valid(tn * BN);
+        else fetch(tn * BN);
+      } else if (ES == 4 && first_far >= 0) {
+        fetch_valid(first_far * BN);   // the register-staged far phase's first tile
+      }
     }
     __syncthreads();  // K, V^T (and c_j) of this tile staged
 
@@ -926,18 +1016,138 @@ void dattn_fwd_kernel(FwdParams p) {
         if (p2c_mode == TERM_BAND && kb + 1 < C::NKB) __syncthreads();  // F reused
       }
     }
-    softmax_pv(s, a_off, v_base0);
+    softmax_pv(s, a_off, vop_staged(v_base0));
     __syncthreads();  // tile buffers free for the next key tile
   }
 
-  // ---- phase 2: far tiles, double-buffered ----------------------------------
-  if (first_far >= 0) {
+  // ---- phase 2 (16-bit types): far tiles through the LDS ring -------------
+  // Far tiles 0..FL-1 and FR..tm-1 are numbered n = 0, 1, ...; tile n lives
+  // in ring slot n % NSTAGE. Loads run three tiles ahead; c_j of tile n+1 is
+  // formed (by MFMA, 16 keys per wave) while tile n is computed; one barrier
+  // per tile publishes both.
+  if constexpr (ES == 2) {
+    const int nfar = FL + max(tm - FR, 0);
+    if (nfar > 0) {
+      auto far_tile = [&](int n) { return n < FL ? n : FR + (n - FL); };
+      const uint32_t ring = (uint32_t)(size_t)(__attribute__((address_space(3))) unsigned char*)smem;
+      constexpr int DPW = C::DMA_PER_WAVE;
+      constexpr int NDMA = 2 * DPW;   // loads of one tile issued by one wave
+      constexpr int ROWB = C::UPR * 16;   // bytes of one ring row
+      // source offsets of this wave's loads (unit order swizzled per row)
+      uint32_t kdo[DPW], vdo[DPW];
+#pragma unroll
+      for (int x = 0; x < DPW; ++x) {
+        const int u_lds = 64 * (wave * DPW + x) + lane;
+        const int r = u_lds / C::UPR, pu = u_lds % C::UPR;
+        kdo[x] = (uint32_t)((r * p.ld_k + hoff) * ES + 16 * (pu ^ C::swz_k(r)));
+        vdo[x] = (uint32_t)((r * p.ld_v + hoff) * ES + 16 * (pu ^ C::swz_v(r)));
+      }
+      auto issue = [&](int n) {
+        const int64_t j0 = far_tile(n) * BN;
+        const unsigned char* kt = Kg + (base + j0) * p.ld_k * ES;
+        const unsigned char* vt = Vg + (base + j0) * p.ld_v * ES;
+        const uint32_t slot = ring + (n % C::NSTAGE) * C::SLOT_BYTES + 1024 * wave * DPW;
+#pragma unroll
+        for (int x = 0; x < DPW; ++x) dma16(slot + 1024 * x, kt, kdo[x]);
+#pragma unroll
+        for (int x = 0; x < DPW; ++x) dma16(slot + C::KT_BYTES + 1024 * x, vt, vdo[x]);
+      };
+      // wait for every tile but the newest k issued ones
+      auto wait_all_but = [&](int k) {
+        if (k <= 0) wait_vm<0>();
+        else if (k == 1) wait_vm<NDMA>();
+        else wait_vm<2 * NDMA>();
+      };
+
+      // c_j of a ring tile: keys 16*wave.. by the 16x16x32 MFMA against a B
+      // operand whose column 0 is qr[top row] and column 1 qr[bottom row]
+      typename Ty<T>::frag cq[D / 32];
+#pragma unroll
+      for (int m = 0; m < D / 32; ++m) {
+        uint4 x = make_uint4(0, 0, 0, 0);
+        if ((lane & 15) < 2)
+          x = ld16(Rrows + ((lane & 15) * D + 32 * m + 8 * (lane >> 4)) * ES);
+        cq[m] = __builtin_bit_cast(typename Ty<T>::frag, x);
+      }
+      auto compute_c = [&](int n) {
+        const int which = far_tile(n) < FL ? 1 : 0;
+        const unsigned char* ks = smem + (n % C::NSTAGE) * C::SLOT_BYTES;
+        const int r = 16 * wave + (lane & 15);
+        f32x4_t acc = f32x4_t{};
+#pragma unroll
+        for (int m = 0; m < D / 32; ++m) {
+          const int u = 4 * m + (lane >> 4);
+          const auto a = __builtin_bit_cast(typename Ty<T>::frag,
+                                            ld16(ks + r * ROWB + 16 * (u ^ C::swz_k(r))));
+          acc = Ty<T>::mma16(a, cq[m], acc);
+        }
+        // lane l holds column l % 16 and keys 16*wave + 4*(l/16) + 0..3
+        if ((lane & 15) == which)
+          *reinterpret_cast<f32x4_t*>(cring + (n & 1) * BN + 16 * wave + 4 * (lane >> 4)) = acc;
+      };
+
+      // per-lane operand offsets inside a slot
+      uint32_t kro[NU];   // K rows li (+32 kb), units lh*NU + x
+#pragma unroll
+      for (int x = 0; x < NU; ++x) kro[x] = li * ROWB + 16 * ((lh * NU + x) ^ C::swz_k(li));
+      const int vg = lane >> 4, vt4 = lane & 15;
+      const int vkey = 4 * (vg >> 1) + (vt4 >> 2);   // + 32 kb + 16 c + 8 h
+      uint32_t vro[C::NDB];
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+        const int u = 4 * db + 2 * (vg & 1) + ((vt4 & 3) >> 1);
+        vro[db] = vkey * ROWB + 16 * (u ^ C::swz_v(vkey)) + 8 * (vt4 & 1);
+      }
+
+      const int npre = min(nfar, C::NSTAGE - 1);
+      for (int n = 0; n < npre; ++n) issue(n);
+      wait_all_but(npre - 1);
+      __syncthreads();  // tile 0 in LDS
+      if (has_p2c) compute_c(0);
+      if (nfar > 1) wait_all_but(npre - 2);
+      __syncthreads();  // c_j of tile 0 and tile 1 visible
+
+      for (int n = 0; n < nfar; ++n) {
+        if (n + C::NSTAGE - 1 < nfar) issue(n + C::NSTAGE - 1);   // into the slot of tile n-1
+        if (has_p2c && n + 1 < nfar) compute_c(n + 1);
+        const int t = far_tile(n);
+        const float a_off = has_c2p ? (t < FL ? a_top : a_bot) : 0.f;
+        const unsigned char* ks = smem + (n % C::NSTAGE) * C::SLOT_BYTES;
+        const unsigned char* vs = ks + C::KT_BYTES;
+        const float* cb = cring + (n & 1) * BN;
+        f32x16_t s[C::NKB];
+        {
+          uint4 kf[C::NKB][NU];
+#pragma unroll
+          for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+            for (int x = 0; x < NU; ++x) kf[kb][x] = ld16(ks + kro[x] + kb * 32 * ROWB);
+#pragma unroll
+          for (int kb = 0; kb < C::NKB; ++kb) {
+            f32x16_t acc = f32x16_t{};
+            if (has_p2c) acc = c_init(cb, kb);
+            s[kb] = mma_chain<T, NU, NC>(kf[kb], qf, acc);
+          }
+        }
+        softmax_pv(s, a_off, [&](int kb, int c, int db) {
+          const unsigned char* a0 = vs + vro[db] + (32 * kb + 16 * c) * ROWB;
+          const uint2 lo = lds_tr16(a0), hi = lds_tr16(a0 + 8 * ROWB);
+          return __builtin_bit_cast(typename Ty<T>::frag, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        });
+        if (n + 2 < nfar) wait_all_but(n + C::NSTAGE - 1 < nfar ? 1 : 0);
+        __syncthreads();  // tile n+2 and c_j of n+1 visible; slot of tile n free
+      }
+    }
+  }
+
+  // ---- phase 2 (fp32): far tiles, double-buffered through registers --------
+  if (ES == 4 && first_far >= 0) {
     // which qr row the constant P2C term reads, and the C2P offset, per side
     auto p2c_row_of = [&](int t) { return has_p2c ? (t < FL ? 1 : 0) : -1; };
     int t = first_far;
     stage(Ks, Vt, cbuf, p2c_row_of(t));
     int tn = next_far(t);
-    if (tn >= 0) fetch(tn * BN);
+    if (tn >= 0) fetch_valid(tn * BN);
     __syncthreads();
     int b = 0;
     while (t >= 0) {
@@ -947,13 +1157,13 @@ void dattn_fwd_kernel(FwdParams p) {
         // wave has finished (barrier at the end of the previous iteration)
         if (b) stage(Ks, Vt, cbuf, p2c_row_of(tn));
         else stage(Ks1, Vt1, cbuf1, p2c_row_of(tn));
-        if (tnn >= 0) fetch(tnn * BN);
+        if (tnn >= 0) fetch_valid(tnn * BN);
       }
       const float a_off = has_c2p ? (t < FL ? a_top : a_bot) : 0.f;
       f32x16_t s[C::NKB];
       if (has_p2c) far_scores(s, b ? Ks1 : Ks, b ? cbuf1 : cbuf, std::true_type{});
       else far_scores(s, b ? Ks1 : Ks, b ? cbuf1 : cbuf, std::false_type{});
-      softmax_pv(s, a_off, b ? v_base1 : v_base0);
+      softmax_pv(s, a_off, vop_staged(b ? v_base1 : v_base0));
       __syncthreads();  // next tile staged; this tile's buffer free
       t = tn;
       tn = tnn;
