@@ -509,11 +509,13 @@ void dattn_fwd_kernel(FwdParams p) {
   // row of qr / kr for a signed distance: beyond the saturation thresholds
   // the table's end rows, inside them the window staged in LDS (or the
   // table itself when the window is too long to stage)
-  auto rel_row = [&](int dist) -> int {
+  // (twok: the window is staged; the two cases are separate instantiations of
+  // the general-tile loop, so the common one never waits on a global load)
+  auto rel_row = [&](int dist, auto twok) -> int {
     int r;
     if (dist <= sat_bot) r = row_lo;
     else if (dist >= sat_top) r = row_hi;
-    else if (tw_ok) r = Tw[dist - sat_bot - 1];
+    else if constexpr (decltype(twok)::value) r = Tw[dist - sat_bot - 1];
     else {
       int x = dist + R - 1;
       x = x < 0 ? 0 : (x > tbl_n - 1 ? tbl_n - 1 : x);
@@ -596,13 +598,11 @@ void dattn_fwd_kernel(FwdParams p) {
     pr = C::VG_P * pg + lane % C::VG_P;
     return g < C::GROUPS;
   };
-  auto key_ok = [&](int j, bool nm) {
-    bool ok = j < ext;
-    if (ok && nm && j >= first_bad) ok = mrow[j] != 0;
-    return ok;
-  };
+  // Rows of keys past the sequence are never read. Rows of masked keys are
+  // read and zeroed when staged; the tile's mask bytes (key j0 + lane) are
+  // fetched with it, one per lane, and turned into a 64-bit valid-key word.
+  int mbyte = 1;
   auto fetch = [&](int j0) {
-    const bool nm = j0 + BN > key_end;
 #pragma unroll
     for (int s = 0; s < C::JPT; ++s) {
       const int x = tid + s * NT;
@@ -610,9 +610,8 @@ void dattn_fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int j = j0 + 2 * pr + h;
-        pk[s][h] = (x < C::JOBS && key_ok(j, nm))
-                       ? ld16(Kg + ((base + j) * p.ld_k + hoff) * ES + 16 * u)
-                       : make_uint4(0, 0, 0, 0);
+        pk[s][h] = (x < C::JOBS && j < ext) ? ld16(Kg + ((base + j) * p.ld_k + hoff) * ES + 16 * u)
+                                            : make_uint4(0, 0, 0, 0);
       }
     }
 #pragma unroll
@@ -622,10 +621,18 @@ void dattn_fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int j = j0 + 2 * pr + h;
-        pv[s][h] = (live && key_ok(j, nm)) ? ld16(Vg + ((base + j) * p.ld_v + hoff) * ES + 16 * u)
-                                           : make_uint4(0, 0, 0, 0);
+        pv[s][h] = (live && j < ext) ? ld16(Vg + ((base + j) * p.ld_v + hoff) * ES + 16 * u)
+                                     : make_uint4(0, 0, 0, 0);
       }
     }
+    if (!VARLEN && mrow && j0 + BN > key_end) {
+      const int j = j0 + lane;
+      mbyte = (j < ext && j >= first_bad) ? (int)mrow[j] : 1;
+    }
+  };
+  // bit k: key j0 + k exists and is not masked (tile last fetched by fetch)
+  auto tile_valid = [&](int j0) -> uint64_t {
+    return (uint64_t)__ballot(j0 + lane < ext && mbyte != 0);
   };
   // fetch for tiles known to hold only valid keys: a uniform tile base plus
   // per-thread byte offsets that do not change from tile to tile
@@ -661,7 +668,25 @@ void dattn_fwd_kernel(FwdParams p) {
   };
   // stage into the given K / V^T / c_j buffers; cj_which >= 0: also write
   // c_j = k_j . qr[row] (row: 0 top, 1 bottom) of the staged keys
-  auto stage = [&](unsigned char* Ks, unsigned char* Vt, float* cbuf, int cj_which) {
+  // kvalid: valid keys of the tile (all ones: nothing to zero)
+  auto stage = [&](unsigned char* Ks, unsigned char* Vt, float* cbuf, int cj_which, uint64_t kvalid) {
+    const bool zero_rows = kvalid != ~0ull;   // uniform
+    auto keep = [&](int k) { return ((kvalid >> k) & 1ull) != 0; };
+    if (zero_rows) {
+#pragma unroll
+      for (int s = 0; s < C::JPT; ++s) {
+        const int pr = (tid + s * NT) / C::UPR;
+        if (!keep(2 * pr)) pk[s][0] = make_uint4(0, 0, 0, 0);
+        if (!keep(2 * pr + 1)) pk[s][1] = make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int s = 0; s < C::GPW; ++s) {
+        int pr, u;
+        vjob_of(s, pr, u);
+        if (!keep(2 * pr)) pv[s][0] = make_uint4(0, 0, 0, 0);
+        if (!keep(2 * pr + 1)) pv[s][1] = make_uint4(0, 0, 0, 0);
+      }
+    }
 #pragma unroll
     for (int s = 0; s < C::JPT; ++s) {
       const int x = tid + s * NT;
@@ -891,29 +916,91 @@ void dattn_fwd_kernel(FwdParams p) {
   const int first_far = FL > 0 ? 0 : (FR < tm ? FR : -1);
 
   // ---- phase 1: general tiles (band products, masks) ------------------------
-  if (first_general >= 0) fetch(first_general * BN);
-  else if (ES == 4 && first_far >= 0) fetch(first_far * BN);
-  for (int t = first_general; t >= 0; t = next_general(t)) {
-    const int j0 = t * BN;
-    const bool need_mask = j0 + BN > key_end;
-
-    // path of each position term for this tile
-    const int k_lo = j0, k_hi = min(j0 + BN, ext) - 1;
-    int p2c_mode = TERM_OFF, p2c_which = 0;   // which: 0 top row, 1 bottom row
+  auto phase1 = [&](auto twok) {
+  // path of each position term for a general tile
+  auto modes_of = [&](int t, int& p2c_mode, int& p2c_which, int& c2p_mode, float& a_off) {
+    const int k_lo = t * BN, k_hi = min(t * BN + BN, ext) - 1;
+    p2c_mode = TERM_OFF;
+    p2c_which = 0;   // which: 0 top row, 1 bottom row
     if (has_p2c) {
       if (k_lo - wg_qhi >= sat_top) { p2c_mode = TERM_CONST; p2c_which = 0; }
       else if (k_hi - wg_qlo <= sat_bot) { p2c_mode = TERM_CONST; p2c_which = 1; }
       else p2c_mode = TERM_BAND;
     }
-    int c2p_mode = TERM_OFF;
-    float a_off = 0.f;
+    c2p_mode = TERM_OFF;
+    a_off = 0.f;
     if (has_c2p && w_qlo <= w_qhi) {
       if (w_qlo - k_hi >= sat_top) { c2p_mode = TERM_CONST; a_off = a_top; }
       else if (w_qhi - k_lo <= sat_bot) { c2p_mode = TERM_CONST; a_off = a_bot; }
       else c2p_mode = TERM_BAND;
     }
+  };
 
-    stage(Ks, Vt, cbuf, p2c_mode == TERM_CONST ? p2c_which : -1);
+  // Band operand rows of one 32-key half: qr rows of the F blocks this wave
+  // computes and kr rows of its two E blocks. With 16-bit types and d <= 64
+  // they are held in registers and fetched one half ahead, right after the
+  // previous half's band products have consumed them, so their latency is
+  // hidden behind the gathers, the Q.K product and (across tiles) P.V.
+  constexpr int FB = (C::NBV + NW - 1) / NW;   // F blocks of one wave
+  constexpr bool PIPE = ES == 2 && D <= 64;
+  uint4 rowF[PIPE ? FB : 1][NU], rowE[PIPE ? 2 : 1][NU];
+  auto load_rows = [&](int t, int kb, int p2c_mode, int c2p_mode) {
+    if constexpr (PIPE) {
+      const int jb = t * BN + 32 * kb;
+      if (p2c_mode == TERM_BAND) {
+        const int vmin = jb - (i0 + BM - 1);
+#pragma unroll
+        for (int x = 0; x < FB; ++x) {
+          const int vb = wave + NW * x;
+          if (vb < C::NBV)
+            load_half_row<NU>(rowF[x], QRg + ((int64_t)rel_row(vmin + vb * 32 + li, twok) * p.ld_rel + hoff +
+                                              lh * C::HALF) * ES);
+        }
+      }
+      if (c2p_mode == TERM_BAND) {
+        const int umin = i0w - (jb + 31);
+#pragma unroll
+        for (int ub = 0; ub < 2; ++ub)
+          load_half_row<NU>(rowE[ub], KRg + ((int64_t)rel_row(umin + ub * 32 + li, twok) * p.ld_rel + hoff +
+                                             lh * C::HALF) * ES);
+      }
+    }
+  };
+  // after the band products of half kb of tile t: fetch the rows of the next half
+  auto load_next_rows = [&](int t, int kb, int p2c_mode, int c2p_mode) {
+    if constexpr (PIPE) {
+      if (kb + 1 < C::NKB) {
+        load_rows(t, kb + 1, p2c_mode, c2p_mode);
+      } else {
+        const int tn = next_general(t);
+        if (tn >= 0) {
+          int pm, pw, cm;
+          float ao;
+          modes_of(tn, pm, pw, cm, ao);
+          load_rows(tn, 0, pm, cm);
+        }
+      }
+    }
+  };
+
+  if (first_general >= 0) {
+    fetch(first_general * BN);
+    int pm, pw, cm;
+    float ao;
+    modes_of(first_general, pm, pw, cm, ao);
+    load_rows(first_general, 0, pm, cm);
+  } else if (ES == 4 && first_far >= 0) {
+    fetch(first_far * BN);
+  }
+  for (int t = first_general; t >= 0; t = next_general(t)) {
+    const int j0 = t * BN;
+    const bool need_mask = j0 + BN > key_end;
+    int p2c_mode, p2c_which, c2p_mode;
+    float a_off;
+    modes_of(t, p2c_mode, p2c_which, c2p_mode, a_off);
+
+    const uint64_t kvalid = need_mask ? tile_valid(j0) : ~0ull;
+    stage(Ks, Vt, cbuf, p2c_mode == TERM_CONST ? p2c_which : -1, kvalid);
     {
       const int tn = next_general(t);
       if (tn >= 0) {
@@ -930,6 +1017,7 @@ void dattn_fwd_kernel(FwdParams p) {
     if (far_tile) {
       if (p2c_mode == TERM_CONST) far_scores(s, Ks, cbuf, std::true_type{});
       else far_scores(s, Ks, cbuf, std::false_type{});
+      load_next_rows(t, C::NKB - 1, p2c_mode, c2p_mode);
     } else {
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb) {
@@ -944,10 +1032,34 @@ void dattn_fwd_kernel(FwdParams p) {
           else return mma_chain<T, NU, NC>(kf, b, acc);
         };
 
-        if (p2c_mode == TERM_BAND) {
+        if constexpr (PIPE) {
+          // F[jh][v] = k_(j0+32kb+jh) . qr[T(vmin + v)], v over BM+31 distances
+          if (p2c_mode == TERM_BAND) {
+#pragma unroll
+            for (int x = 0; x < FB; ++x) {
+              const int vb = wave + NW * x;
+              if (vb < C::NBV) {
+                const f32x16_t f = kchain(rowF[x], f32x16_t{});
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                  Fw[(rr_of(r) + 4 * lh) * C::FWP + vb * 32 + li] = f[r];
+              }
+            }
+          }
+          // E[u][i] = kr[T(umin + u)] . q_i, u over the wave's 63 distances
+          if (c2p_mode == TERM_BAND) {
+#pragma unroll
+            for (int ub = 0; ub < 2; ++ub) {
+              const f32x16_t e = mma_chain<T, NU, NC>(rowE[ub], qf, f32x16_t{});
+#pragma unroll
+              for (int r = 0; r < 16; ++r) Eww[(ub * 32 + rr_of(r) + 4 * lh) * 32 + li] = e[r];
+            }
+          }
+          load_next_rows(t, kb, p2c_mode, c2p_mode);
+        }
+        if (!PIPE && p2c_mode == TERM_BAND) {
           // F[jh][v] = k_(j0+32kb+jh) . qr[T(vmin + v)], v over BM+31 distances
           const int vmin = (j0 + 32 * kb) - (i0 + BM - 1);
-          constexpr int FB = (C::NBV + NW - 1) / NW;   // F blocks of one wave
           constexpr int FL = WIDE ? 1 : FB;             // blocks loaded together
 #pragma unroll
           for (int t0 = 0; t0 < FB; t0 += FL) {
@@ -956,7 +1068,7 @@ void dattn_fwd_kernel(FwdParams p) {
             for (int t = 0; t < FL; ++t) {
               const int vb = wave + NW * (t0 + t);
               if (vb < C::NBV)
-                load_half_row<NU>(rf[t], QRg + ((int64_t)rel_row(vmin + vb * 32 + li) * p.ld_rel +
+                load_half_row<NU>(rf[t], QRg + ((int64_t)rel_row(vmin + vb * 32 + li, twok) * p.ld_rel +
                                                 hoff + lh * C::HALF) * ES);
             }
 #pragma unroll
@@ -971,7 +1083,7 @@ void dattn_fwd_kernel(FwdParams p) {
             }
           }
         }
-        if (c2p_mode == TERM_BAND) {
+        if (!PIPE && c2p_mode == TERM_BAND) {
           // E[u][i] = kr[T(umin + u)] . q_i, u over the wave's 63 distances
           const int umin = i0w - (j0 + 32 * kb + 31);
           constexpr int EL = WIDE ? 1 : 2;              // blocks loaded together
@@ -980,7 +1092,7 @@ void dattn_fwd_kernel(FwdParams p) {
             uint4 rf[EL][NU];
 #pragma unroll
             for (int ub = 0; ub < EL; ++ub)
-              load_half_row<NU>(rf[ub], KRg + ((int64_t)rel_row(umin + (u0 + ub) * 32 + li) *
+              load_half_row<NU>(rf[ub], KRg + ((int64_t)rel_row(umin + (u0 + ub) * 32 + li, twok) *
                                                    p.ld_rel + hoff + lh * C::HALF) * ES);
 #pragma unroll
             for (int ub = 0; ub < EL; ++ub) {
@@ -1004,13 +1116,10 @@ void dattn_fwd_kernel(FwdParams p) {
           for (int r = 0; r < 16; ++r) acc[r] += f_base[rr_of(r) * (C::FWP + 1)];
         }
         if (need_mask) {
+          const uint32_t kv = (uint32_t)(kvalid >> (kb * 32 + 4 * lh));   // this lane's keys
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = j0 + kb * 32 + rr_of(r) + 4 * lh;
-            bool ok = j < ext;
-            if (ok && j >= first_bad) ok = mrow[j] != 0;
-            if (!ok) acc[r] = NEG_INF;
-          }
+          for (int r = 0; r < 16; ++r)
+            if (!((kv >> rr_of(r)) & 1u)) acc[r] = NEG_INF;
         }
         s[kb] = acc;
         if (p2c_mode == TERM_BAND && kb + 1 < C::NKB) __syncthreads();  // F reused
@@ -1019,6 +1128,10 @@ void dattn_fwd_kernel(FwdParams p) {
     softmax_pv(s, a_off, vop_staged(v_base0));
     __syncthreads();  // tile buffers free for the next key tile
   }
+
+  };
+  if (tw_ok) phase1(std::true_type{});
+  else phase1(std::false_type{});
 
   // ---- phase 2 (16-bit types): far tiles through the LDS ring -------------
   // Far tiles 0..FL-1 and FR..tm-1 are numbered n = 0, 1, ...; tile n lives
@@ -1145,7 +1258,7 @@ void dattn_fwd_kernel(FwdParams p) {
     // which qr row the constant P2C term reads, and the C2P offset, per side
     auto p2c_row_of = [&](int t) { return has_p2c ? (t < FL ? 1 : 0) : -1; };
     int t = first_far;
-    stage(Ks, Vt, cbuf, p2c_row_of(t));
+    stage(Ks, Vt, cbuf, p2c_row_of(t), ~0ull);
     int tn = next_far(t);
     if (tn >= 0) fetch_valid(tn * BN);
     __syncthreads();
@@ -1155,8 +1268,8 @@ void dattn_fwd_kernel(FwdParams p) {
       if (tn >= 0) {
         // the other buffer was last read by the previous tile, which every
         // wave has finished (barrier at the end of the previous iteration)
-        if (b) stage(Ks, Vt, cbuf, p2c_row_of(tn));
-        else stage(Ks1, Vt1, cbuf1, p2c_row_of(tn));
+        if (b) stage(Ks, Vt, cbuf, p2c_row_of(tn), ~0ull);
+        else stage(Ks1, Vt1, cbuf1, p2c_row_of(tn), ~0ull);
         if (tnn >= 0) fetch_valid(tnn * BN);
       }
       const float a_off = has_c2p ? (t < FL ? a_top : a_bot) : 0.f;
