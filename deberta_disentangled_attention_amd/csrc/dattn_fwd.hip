@@ -1212,17 +1212,20 @@ void dattn_fwd_kernel(FwdParams p) {
         vro[db] = vkey * ROWB + 16 * (u ^ C::swz_v(vkey)) + 8 * (vt4 & 1);
       }
 
+      // the loop is instantiated with and without the P2C term
+      auto ring_loop = [&](auto pc) {
+      constexpr bool PC = decltype(pc)::value;
       const int npre = min(nfar, C::NSTAGE - 1);
       for (int n = 0; n < npre; ++n) issue(n);
       wait_all_but(npre - 1);
       __syncthreads();  // tile 0 in LDS
-      if (has_p2c) compute_c(0);
+      if constexpr (PC) compute_c(0);
       if (nfar > 1) wait_all_but(npre - 2);
       __syncthreads();  // c_j of tile 0 and tile 1 visible
 
       for (int n = 0; n < nfar; ++n) {
         if (n + C::NSTAGE - 1 < nfar) issue(n + C::NSTAGE - 1);   // into the slot of tile n-1
-        if (has_p2c && n + 1 < nfar) compute_c(n + 1);
+        if (PC && n + 1 < nfar) compute_c(n + 1);
         const int t = far_tile(n);
         const float a_off = has_c2p ? (t < FL ? a_top : a_bot) : 0.f;
         const unsigned char* ks = smem + (n % C::NSTAGE) * C::SLOT_BYTES;
@@ -1238,7 +1241,7 @@ void dattn_fwd_kernel(FwdParams p) {
 #pragma unroll
           for (int kb = 0; kb < C::NKB; ++kb) {
             f32x16_t acc = f32x16_t{};
-            if (has_p2c) acc = c_init(cb, kb);
+            if constexpr (PC) acc = c_init(cb, kb);
             s[kb] = mma_chain<T, NU, NC>(kf[kb], qf, acc);
           }
         }
@@ -1250,6 +1253,9 @@ void dattn_fwd_kernel(FwdParams p) {
         if (n + 2 < nfar) wait_all_but(n + C::NSTAGE - 1 < nfar ? 1 : 0);
         __syncthreads();  // tile n+2 and c_j of n+1 visible; slot of tile n free
       }
+      };
+      if (has_p2c) ring_loop(std::true_type{});
+      else ring_loop(std::false_type{});
     }
   }
 
