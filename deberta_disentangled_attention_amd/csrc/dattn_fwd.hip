@@ -173,8 +173,8 @@ struct Cfg {
   static constexpr int RING_BYTES = ES == 2 ? NSTAGE * SLOT_BYTES : 0;
   static constexpr int P1_BYTES = OFF_F + F_BYTES;
   static constexpr int OFF_C = P1_BYTES > RING_BYTES ? P1_BYTES : RING_BYTES;
-  static constexpr int OFF_CR = OFF_C + C_BYTES;     // c_j of two ring tiles
-  static constexpr int OFF_R = OFF_CR + 2 * C_BYTES;
+  static constexpr int OFF_CR = OFF_C + C_BYTES;     // c_j of three ring tiles
+  static constexpr int OFF_R = OFF_CR + 3 * C_BYTES;
   static constexpr int OFF_TW = OFF_R + R_BYTES;
   static constexpr int OFF_MISC = OFF_TW + TW_BYTES;
   static constexpr int LDS_BYTES = OFF_MISC + 64;
@@ -792,7 +792,9 @@ void dattn_fwd_kernel(FwdParams p) {
   // online softmax of a tile's scores and O^T += V^T P^T
   // vop(kb, c, db): V^T operand of the P.V MFMA for key block kb, 16-key
   // group c (16-bit types) or 8-key group c (fp32), head-dim block db
-  auto softmax_pv = [&](f32x16_t (&s)[C::NKB], float a_off, auto vop) {
+  // mid(): work issued after the rescale decision and before the
+  // exponentials (the next tile's Q.K MFMAs in the pipelined far loop)
+  auto softmax_pv_mid = [&](f32x16_t (&s)[C::NKB], float a_off, auto vop, auto mid) {
     // P for the P.V MFMA, already rounded to the element type (16-bit types)
     typename Ty<T>::frag pfrag[ES == 2 ? C::NKB : 1][2];
     // ---- online softmax (base 2, scale folded) ---------------------------
@@ -832,6 +834,7 @@ void dattn_fwd_kernel(FwdParams p) {
         for (int x = 0; x < C::NDB; ++x) o_acc[x] *= alpha;
         m_run = m_new;
       }
+      mid();
       const float bias = off - (m_run == NEG_INF ? 0.f : m_run);
       float ps4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -886,6 +889,9 @@ void dattn_fwd_kernel(FwdParams p) {
       }
     }
 
+  };
+  auto softmax_pv = [&](f32x16_t (&s)[C::NKB], float a_off, auto vop) {
+    softmax_pv_mid(s, a_off, vop, [] {});
   };
 
   // ---- tile classes -------------------------------------------------------
@@ -1196,7 +1202,7 @@ void dattn_fwd_kernel(FwdParams p) {
         }
         // lane l holds column l % 16 and keys 16*wave + 4*(l/16) + 0..3
         if ((lane & 15) == which)
-          *reinterpret_cast<f32x4_t*>(cring + (n & 1) * BN + 16 * wave + 4 * (lane >> 4)) = acc;
+          *reinterpret_cast<f32x4_t*>(cring + (n % 3) * BN + 16 * wave + 4 * (lane >> 4)) = acc;
       };
 
       // per-lane operand offsets inside a slot
@@ -1212,47 +1218,67 @@ void dattn_fwd_kernel(FwdParams p) {
         vro[db] = vkey * ROWB + 16 * (u ^ C::swz_v(vkey)) + 8 * (vt4 & 1);
       }
 
-      // the loop is instantiated with and without the P2C term
+      // The loop is instantiated with and without the P2C term. It is
+      // software-pipelined: the scores of tile n+1 are produced by MFMAs
+      // issued inside tile n's softmax, after its rescale decision, so they
+      // overlap its exponentials; c_j runs two tiles ahead so that those
+      // scores never wait for another wave.
       auto ring_loop = [&](auto pc) {
-      constexpr bool PC = decltype(pc)::value;
-      const int npre = min(nfar, C::NSTAGE - 1);
-      for (int n = 0; n < npre; ++n) issue(n);
-      wait_all_but(npre - 1);
-      __syncthreads();  // tile 0 in LDS
-      if constexpr (PC) compute_c(0);
-      if (nfar > 1) wait_all_but(npre - 2);
-      __syncthreads();  // c_j of tile 0 and tile 1 visible
-
-      for (int n = 0; n < nfar; ++n) {
-        if (n + C::NSTAGE - 1 < nfar) issue(n + C::NSTAGE - 1);   // into the slot of tile n-1
-        if (PC && n + 1 < nfar) compute_c(n + 1);
-        const int t = far_tile(n);
-        const float a_off = has_c2p ? (t < FL ? a_top : a_bot) : 0.f;
-        const unsigned char* ks = smem + (n % C::NSTAGE) * C::SLOT_BYTES;
-        const unsigned char* vs = ks + C::KT_BYTES;
-        const float* cb = cring + (n & 1) * BN;
-        f32x16_t s[C::NKB];
-        {
-          uint4 kf[C::NKB][NU];
-#pragma unroll
-          for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-            for (int x = 0; x < NU; ++x) kf[kb][x] = ld16(ks + kro[x] + kb * 32 * ROWB);
+        constexpr bool PC = decltype(pc)::value;
+        auto scores = [&](int n, f32x16_t (&s)[C::NKB]) {
+          const unsigned char* ks = smem + (n % C::NSTAGE) * C::SLOT_BYTES;
+          const float* cb = cring + (n % 3) * BN;
 #pragma unroll
           for (int kb = 0; kb < C::NKB; ++kb) {
+            uint4 kf[NU];
+#pragma unroll
+            for (int x = 0; x < NU; ++x) kf[x] = ld16(ks + kro[x] + kb * 32 * ROWB);
             f32x16_t acc = f32x16_t{};
             if constexpr (PC) acc = c_init(cb, kb);
-            s[kb] = mma_chain<T, NU, NC>(kf[kb], qf, acc);
+            s[kb] = mma_chain<T, NU, NC>(kf, qf, acc);
           }
+        };
+        // tile n: scores in s_cur; produces the scores of tile n+1 in s_nxt
+        auto step = [&](int n, f32x16_t (&s_cur)[C::NKB], f32x16_t (&s_nxt)[C::NKB]) {
+          if (n + C::NSTAGE - 1 < nfar) issue(n + C::NSTAGE - 1);   // into the slot of tile n-1
+          if (PC && n + 2 < nfar) compute_c(n + 2);
+          const int t = far_tile(n);
+          const float a_off = has_c2p ? (t < FL ? a_top : a_bot) : 0.f;
+          const unsigned char* vs = smem + (n % C::NSTAGE) * C::SLOT_BYTES + C::KT_BYTES;
+          softmax_pv_mid(
+              s_cur, a_off,
+              [&](int kb, int c, int db) {
+                const unsigned char* a0 = vs + vro[db] + (32 * kb + 16 * c) * ROWB;
+                const uint2 lo = lds_tr16(a0), hi = lds_tr16(a0 + 8 * ROWB);
+                return __builtin_bit_cast(typename Ty<T>::frag, make_uint4(lo.x, lo.y, hi.x, hi.y));
+              },
+              // unconditional, so the MFMAs share a block with the
+              // exponentials; after the last tile they read a stale slot
+              // and their result is not used
+              [&] { scores(n + 1, s_nxt); });
+          // all of this wave's loads done: tile n+3 (and c_j of n+2) are
+          // visible after the barrier, and the slot of tile n is free
+          wait_vm<0>();
+          __syncthreads();
+        };
+
+        const int npre = min(nfar, C::NSTAGE - 1);
+        for (int n = 0; n < npre; ++n) issue(n);
+        wait_vm<0>();
+        __syncthreads();  // tiles 0 .. npre-1 in LDS
+        if constexpr (PC) {
+          compute_c(0);
+          if (nfar > 1) compute_c(1);
+          __syncthreads();  // c_j of tiles 0 and 1 visible
         }
-        softmax_pv(s, a_off, [&](int kb, int c, int db) {
-          const unsigned char* a0 = vs + vro[db] + (32 * kb + 16 * c) * ROWB;
-          const uint2 lo = lds_tr16(a0), hi = lds_tr16(a0 + 8 * ROWB);
-          return __builtin_bit_cast(typename Ty<T>::frag, make_uint4(lo.x, lo.y, hi.x, hi.y));
-        });
-        if (n + 2 < nfar) wait_all_but(n + C::NSTAGE - 1 < nfar ? 1 : 0);
-        __syncthreads();  // tile n+2 and c_j of n+1 visible; slot of tile n free
-      }
+        f32x16_t sa[C::NKB], sb[C::NKB];
+        scores(0, sa);
+        int n = 0;
+        for (; n + 1 < nfar; n += 2) {
+          step(n, sa, sb);
+          step(n + 1, sb, sa);
+        }
+        if (n < nfar) step(n, sa, sb);
       };
       if (has_p2c) ring_loop(std::true_type{});
       else ring_loop(std::false_type{});
