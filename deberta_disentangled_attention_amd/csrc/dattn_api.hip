@@ -37,6 +37,7 @@ int check_common(const void* q, const void* k, const void* v, int64_t ld_q, int6
     if (n_rel < 1 || ld_rel < hd) return DATTN_ERR_INVALID_ARGUMENT;
     if (rel_max_len < seq_bound || rel_max_len < 1) return DATTN_ERR_INVALID_ARGUMENT;
     if (!aligned16(qr) || !aligned16(kr) || (ld_rel * es) % 16) return DATTN_ERR_UNSUPPORTED;
+    if ((int64_t)n_rel * ld_rel * es > INT32_MAX) return DATTN_ERR_UNSUPPORTED;  // row offsets are 31-bit
   }
   return DATTN_OK;
 }

@@ -171,8 +171,17 @@ struct Cfg {
   static constexpr int KT_BYTES = BN * UPR * 16;
   static constexpr int SLOT_BYTES = 2 * KT_BYTES;
   static constexpr int RING_BYTES = ES == 2 ? NSTAGE * SLOT_BYTES : 0;
-  static constexpr int P1_BYTES = OFF_F + F_BYTES;
-  static constexpr int OFF_C = P1_BYTES > RING_BYTES ? P1_BYTES : RING_BYTES;
+  // general tiles of 16-bit types: two slots of the ring's layout, then the
+  // per-wave scratch of the band products (E: 64 distances x 32 queries, F:
+  // 32 keys x 64 distances, fp32) and of the per-wave c_j
+  static constexpr int SCR_BYTES = 64 * 32 * 4;
+  static constexpr int OFF_SCR = 2 * SLOT_BYTES;
+  static constexpr int OFF_CJW = OFF_SCR + NW * SCR_BYTES;
+  static constexpr int G16_BYTES = ES == 2 ? OFF_CJW + NW * BN * 4 : 0;
+  // general tiles of fp32: the register-staged layout above
+  static constexpr int P1_BYTES = ES == 4 ? OFF_F + F_BYTES : 0;
+  static constexpr int P_MAX = P1_BYTES > RING_BYTES ? P1_BYTES : RING_BYTES;
+  static constexpr int OFF_C = P_MAX > G16_BYTES ? P_MAX : G16_BYTES;
   static constexpr int OFF_CR = OFF_C + C_BYTES;     // c_j of three ring tiles
   static constexpr int OFF_R = OFF_CR + 3 * C_BYTES;
   static constexpr int OFF_TW = OFF_R + R_BYTES;
@@ -399,7 +408,7 @@ void dattn_fwd_kernel(FwdParams p) {
   float* cring = reinterpret_cast<float*>(smem + C::OFF_CR);
   unsigned char* Rrows = smem + C::OFF_R;   // qr_top, qr_bot, kr_top, kr_bot
   int* misc = reinterpret_cast<int*>(smem + C::OFF_MISC);
-  int* Tw = reinterpret_cast<int*>(smem + C::OFF_TW);   // table rows for sat_bot < d < sat_top
+  uint32_t* Tw = reinterpret_cast<uint32_t*>(smem + C::OFF_TW);   // row offsets, sat_bot <= d <= sat_top
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -503,25 +512,34 @@ void dattn_fwd_kernel(FwdParams p) {
   const int R = p.rel_max_len;
   const int tbl_n = 2 * R - 1;
   auto clamp_row = [&](int r) { return r < 0 ? 0 : (r >= p.n_rel ? p.n_rel - 1 : r); };
+  // byte offset of a (clamped) relative row; rows times the row stride fit in
+  // 31 bits (checked by the host)
+  const uint32_t ld_rel_b = (uint32_t)(p.ld_rel * ES);
+  auto row_off = [&](int r) { return (uint32_t)clamp_row(r) * ld_rel_b; };
   int sat_top = 1 << 30, sat_bot = -(1 << 30);
   int row_hi = 0, row_lo = 0;
+  int wlen = 0;
   bool tw_ok = false;
-  // row of qr / kr for a signed distance: beyond the saturation thresholds
-  // the table's end rows, inside them the window staged in LDS (or the
-  // table itself when the window is too long to stage)
-  // (twok: the window is staged; the two cases are separate instantiations of
-  // the general-tile loop, so the common one never waits on a global load)
-  auto rel_row = [&](int dist, auto twok) -> int {
-    int r;
-    if (dist <= sat_bot) r = row_lo;
-    else if (dist >= sat_top) r = row_hi;
-    else if constexpr (decltype(twok)::value) r = Tw[dist - sat_bot - 1];
-    else {
-      int x = dist + R - 1;
-      x = x < 0 ? 0 : (x > tbl_n - 1 ? tbl_n - 1 : x);
-      r = p.rel_idx[x];
+  // Byte offset of the qr / kr row of a signed distance. The table is
+  // staged in LDS as offsets for the distances sat_bot .. sat_top (the
+  // end entries stand for everything beyond), or read from global memory
+  // when that window is too long; the two cases are separate instantiations
+  // of the general-tile loops, so the common one never waits on a global
+  // load.
+  auto rel_off = [&](int dist, auto twok) -> uint32_t {
+    if constexpr (decltype(twok)::value) {
+      return Tw[min(max(dist - sat_bot, 0), wlen + 1)];
+    } else {
+      int r;
+      if (dist <= sat_bot) r = row_lo;
+      else if (dist >= sat_top) r = row_hi;
+      else {
+        int x = dist + R - 1;
+        x = x < 0 ? 0 : (x > tbl_n - 1 ? tbl_n - 1 : x);
+        r = p.rel_idx[x];
+      }
+      return row_off(r);
     }
-    return clamp_row(r);
   };
   if (has_c2p || has_p2c) {
     const int32_t* tb = p.rel_idx;
@@ -533,10 +551,11 @@ void dattn_fwd_kernel(FwdParams p) {
         tbl_n, [&](int x) { return tb[x] != row_lo; }, &misc[2], tid);
     sat_top = first_top - (R - 1);
     sat_bot = first_above_bot - 1 - (R - 1);
-    const int wlen = sat_top - sat_bot - 1;
-    tw_ok = wlen <= C::TW;
+    wlen = sat_top - sat_bot - 1;
+    tw_ok = wlen + 2 <= C::TW;
     if (tw_ok)
-      for (int x = tid; x < wlen; x += NT) Tw[x] = tb[sat_bot + 1 + x + R - 1];
+      for (int x = tid; x < wlen + 2; x += NT)
+        Tw[x] = row_off(x == 0 ? row_lo : (x == wlen + 1 ? row_hi : tb[sat_bot + x + R - 1]));
     // stage the two saturation rows of qr and kr (this head) in LDS
     constexpr int RU = D * ES / 16;
     for (int x = tid; x < 4 * RU; x += NT) {
@@ -789,40 +808,43 @@ void dattn_fwd_kernel(FwdParams p) {
     }
   };
 
-  // online softmax of a tile's scores and O^T += V^T P^T
+  // Online softmax of a tile's scores (softmax_p) and O^T += V^T P^T (pv_acc).
+  // softmax_p writes P to pfrag (16-bit types) or over s (fp32).
+  // mid(): MFMA work issued in the same block as the exponentials (in the
+  // pipelined far loop: the previous tile's P.V and a later tile's Q.K).
+  // rescore(s): forms the tile's scores again (far loop), or nullptr.
   // vop(kb, c, db): V^T operand of the P.V MFMA for key block kb, 16-key
-  // group c (16-bit types) or 8-key group c (fp32), head-dim block db
-  // mid(): work issued after the rescale decision and before the
-  // exponentials (the next tile's Q.K MFMAs in the pipelined far loop)
-  auto softmax_pv_mid = [&](f32x16_t (&s)[C::NKB], float a_off, auto vop, auto mid) {
-    // P for the P.V MFMA, already rounded to the element type (16-bit types)
-    typename Ty<T>::frag pfrag[ES == 2 ? C::NKB : 1][2];
+  // group c (16-bit types) or 8-key group c (fp32), head-dim block db.
+  typedef typename Ty<T>::frag PFrag[ES == 2 ? C::NKB : 1][2];
+  auto softmax_p = [&](f32x16_t (&s)[C::NKB], float a_off, PFrag& pfrag, auto mid, auto rescore) {
     // ---- online softmax (base 2, scale folded) ---------------------------
-    // The exponent offset m_run is raised only when the tile maximum exceeds
-    // it by more than 8 (so every p <= 2^8), and the accumulators are then
-    // rescaled by alpha. O and l share the offset, so O / l does not depend
-    // on that choice; after the first tile the raise is rare, and the branch
-    // is laid out as the cold path. For 16-bit types the row sum is taken
-    // from the rounded P the P.V product uses (dot2 against (1, 1)).
+    // The exponent offset m_run follows the row maximum loosely: it is
+    // raised (and the accumulators rescaled by alpha) only when a tile's
+    // maximum exceeds it by more than 8. O and l share the offset, so O / l
+    // does not depend on that choice. For 16-bit types the tile maximum is
+    // not formed on the hot path: the exponentials are taken against the
+    // current offset and their row-half sum, which is at most 32 * 2^8 when
+    // no raise is due, detects a due raise (or an overflow); that rare case
+    // and the first tile (no offset yet) take the cold path, which forms the
+    // maximum and redoes the exponentials. The two lanes of a query always
+    // move m_run together. For 16-bit types the row sum is taken from the
+    // rounded P the P.V product uses (dot2 against (1, 1)).
     {
       const float tl2 = p.scale_log2;
       const float off = a_off * tl2;
-      float mx4[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
+      // raise m_run where this tile's maximum exceeds it by more than 8
+      auto raise_to_max = [&] {
+        float mx4[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
 #pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb)
+        for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; r += 4) {
-          mx4[0] = fmaxf(mx4[0], s[kb][r]);
-          mx4[1] = fmaxf(mx4[1], s[kb][r + 1]);
-          mx4[2] = fmaxf(mx4[2], s[kb][r + 2]);
-          mx4[3] = fmaxf(mx4[3], s[kb][r + 3]);
-        }
-      // This lane's half of the row decides alone whether a raise may be
-      // needed; only then is the maximum of both halves formed, so the two
-      // lanes of a query always move m_run together.
-      const float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
-      const float mt_half = (mx == NEG_INF) ? NEG_INF : fmaf(mx, tl2, off);
-      if (__builtin_expect(__any(mt_half > m_run + 8.f), 0)) {
+          for (int r = 0; r < 16; r += 4) {
+            mx4[0] = fmaxf(mx4[0], s[kb][r]);
+            mx4[1] = fmaxf(mx4[1], s[kb][r + 1]);
+            mx4[2] = fmaxf(mx4[2], s[kb][r + 2]);
+            mx4[3] = fmaxf(mx4[3], s[kb][r + 3]);
+          }
+        const float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
         const float mxf = fmaxf(mx, wave_xor32(mx));
         const float mt = (mxf == NEG_INF) ? NEG_INF : fmaf(mxf, tl2, off);
         const bool raise = mt > m_run + 8.f;
@@ -833,37 +855,75 @@ void dattn_fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int x = 0; x < C::NDB; ++x) o_acc[x] *= alpha;
         m_run = m_new;
-      }
-      mid();
-      const float bias = off - (m_run == NEG_INF ? 0.f : m_run);
-      float ps4[4] = {0.f, 0.f, 0.f, 0.f};
+      };
+      // P = exp2(s * tl2 + bias) (rounded to the element type for 16-bit
+      // types); returns this lane's sum of it
+      auto exps = [&]() -> float {
+        const float bias = off - (m_run == NEG_INF ? 0.f : m_run);
+        float ps4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb)
+        for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-          f32x8_t e8;
+          for (int c2 = 0; c2 < 2; ++c2) {
+            f32x8_t e8;
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            e8[e] = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * c2 + e], tl2, bias));
-          if constexpr (ES == 2) {
-            pfrag[kb][c2] = Ty<T>::cvt8(e8);
-            const uint4 w = __builtin_bit_cast(uint4, pfrag[kb][c2]);
-            ps4[0] = Ty<T>::sum2(w.x, ps4[0]);
-            ps4[1] = Ty<T>::sum2(w.y, ps4[1]);
-            ps4[2] = Ty<T>::sum2(w.z, ps4[2]);
-            ps4[3] = Ty<T>::sum2(w.w, ps4[3]);
-          } else {
+            for (int e = 0; e < 8; ++e)
+              e8[e] = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * c2 + e], tl2, bias));
+            if constexpr (ES == 2) {
+              pfrag[kb][c2] = Ty<T>::cvt8(e8);
+              const uint4 w = __builtin_bit_cast(uint4, pfrag[kb][c2]);
+              ps4[0] = Ty<T>::sum2(w.x, ps4[0]);
+              ps4[1] = Ty<T>::sum2(w.y, ps4[1]);
+              ps4[2] = Ty<T>::sum2(w.z, ps4[2]);
+              ps4[3] = Ty<T>::sum2(w.w, ps4[3]);
+            } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              s[kb][8 * c2 + e] = e8[e];
-              ps4[e & 3] += e8[e];
+              for (int e = 0; e < 8; ++e) {
+                s[kb][8 * c2 + e] = e8[e];
+                ps4[e & 3] += e8[e];
+              }
             }
           }
+        return (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
+      };
+      constexpr bool LAZY = ES == 2 && !std::is_same<decltype(rescore), std::nullptr_t>::value;
+      if constexpr (LAZY) {
+        // rescore(s) forms this tile's scores again, so the scores need not
+        // stay live past the exponentials; mid()'s MFMAs, the exponentials
+        // and the test share one block (a lane with no offset yet always
+        // takes the cold path, after mid()'s P.V has accumulated)
+        mid();
+        float ps = exps();
+        if (__builtin_expect(__any(!(ps <= 32.f * 256.f) || m_run == NEG_INF), 0)) {
+          rescore(s);
+          raise_to_max();
+          ps = exps();
         }
-      l_part += (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
+        l_part += ps;
+      } else {
+        // the tile maximum first: a raise is rare, so only a lane's own half
+        // of the row is tested on the hot path
+        float mx4[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; r += 4) {
+            mx4[0] = fmaxf(mx4[0], s[kb][r]);
+            mx4[1] = fmaxf(mx4[1], s[kb][r + 1]);
+            mx4[2] = fmaxf(mx4[2], s[kb][r + 2]);
+            mx4[3] = fmaxf(mx4[3], s[kb][r + 3]);
+          }
+        const float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
+        const float mt_half = (mx == NEG_INF) ? NEG_INF : fmaf(mx, tl2, off);
+        if (__builtin_expect(__any(mt_half > m_run + 8.f), 0)) raise_to_max();
+        mid();
+        l_part += exps();
+      }
     }
+  };
 
-    // ---- O^T += V^T P^T --------------------------------------------------
+  // O^T += V^T P^T; P in pfrag (16-bit types) or in s (fp32)
+  auto pv_acc = [&](const PFrag& pfrag, f32x16_t (&s)[C::NKB], auto vop) {
 #pragma unroll
     for (int kb = 0; kb < C::NKB; ++kb) {
       if constexpr (ES == 2) {
@@ -888,10 +948,14 @@ void dattn_fwd_kernel(FwdParams p) {
         }
       }
     }
-
+  };
+  auto softmax_pv_mid = [&](f32x16_t (&s)[C::NKB], float a_off, auto vop, auto mid, auto rescore) {
+    PFrag pfrag;
+    softmax_p(s, a_off, pfrag, mid, rescore);
+    pv_acc(pfrag, s, vop);
   };
   auto softmax_pv = [&](f32x16_t (&s)[C::NKB], float a_off, auto vop) {
-    softmax_pv_mid(s, a_off, vop, [] {});
+    softmax_pv_mid(s, a_off, vop, [] {}, nullptr);
   };
 
   // ---- tile classes -------------------------------------------------------
@@ -942,62 +1006,13 @@ void dattn_fwd_kernel(FwdParams p) {
     }
   };
 
-  // Band operand rows of one 32-key half: qr rows of the F blocks this wave
-  // computes and kr rows of its two E blocks. With 16-bit types and d <= 64
-  // they are held in registers and fetched one half ahead, right after the
-  // previous half's band products have consumed them, so their latency is
-  // hidden behind the gathers, the Q.K product and (across tiles) P.V.
   constexpr int FB = (C::NBV + NW - 1) / NW;   // F blocks of one wave
-  constexpr bool PIPE = ES == 2 && D <= 64;
-  uint4 rowF[PIPE ? FB : 1][NU], rowE[PIPE ? 2 : 1][NU];
-  auto load_rows = [&](int t, int kb, int p2c_mode, int c2p_mode) {
-    if constexpr (PIPE) {
-      const int jb = t * BN + 32 * kb;
-      if (p2c_mode == TERM_BAND) {
-        const int vmin = jb - (i0 + BM - 1);
-#pragma unroll
-        for (int x = 0; x < FB; ++x) {
-          const int vb = wave + NW * x;
-          if (vb < C::NBV)
-            load_half_row<NU>(rowF[x], QRg + ((int64_t)rel_row(vmin + vb * 32 + li, twok) * p.ld_rel + hoff +
-                                              lh * C::HALF) * ES);
-        }
-      }
-      if (c2p_mode == TERM_BAND) {
-        const int umin = i0w - (jb + 31);
-#pragma unroll
-        for (int ub = 0; ub < 2; ++ub)
-          load_half_row<NU>(rowE[ub], KRg + ((int64_t)rel_row(umin + ub * 32 + li, twok) * p.ld_rel + hoff +
-                                             lh * C::HALF) * ES);
-      }
-    }
-  };
-  // after the band products of half kb of tile t: fetch the rows of the next half
-  auto load_next_rows = [&](int t, int kb, int p2c_mode, int c2p_mode) {
-    if constexpr (PIPE) {
-      if (kb + 1 < C::NKB) {
-        load_rows(t, kb + 1, p2c_mode, c2p_mode);
-      } else {
-        const int tn = next_general(t);
-        if (tn >= 0) {
-          int pm, pw, cm;
-          float ao;
-          modes_of(tn, pm, pw, cm, ao);
-          load_rows(tn, 0, pm, cm);
-        }
-      }
-    }
-  };
+  // this lane's half of a qr / kr row: base plus the row offset
+  const unsigned char* qr_lane = QRg + (hoff + lh * C::HALF) * ES;
+  const unsigned char* kr_lane = KRg + (hoff + lh * C::HALF) * ES;
 
-  if (first_general >= 0) {
-    fetch(first_general * BN);
-    int pm, pw, cm;
-    float ao;
-    modes_of(first_general, pm, pw, cm, ao);
-    load_rows(first_general, 0, pm, cm);
-  } else if (ES == 4 && first_far >= 0) {
-    fetch(first_far * BN);
-  }
+  if (first_general >= 0) fetch(first_general * BN);
+  else if (first_far >= 0) fetch(first_far * BN);
   for (int t = first_general; t >= 0; t = next_general(t)) {
     const int j0 = t * BN;
     const bool need_mask = j0 + BN > key_end;
@@ -1023,96 +1038,44 @@ void dattn_fwd_kernel(FwdParams p) {
     if (far_tile) {
       if (p2c_mode == TERM_CONST) far_scores(s, Ks, cbuf, std::true_type{});
       else far_scores(s, Ks, cbuf, std::false_type{});
-      load_next_rows(t, C::NKB - 1, p2c_mode, c2p_mode);
     } else {
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb) {
-        // fp32 rows are wide: K is then read from LDS per MFMA instead of
-        // held in registers, and relative rows are fetched one block at a time
-        constexpr bool WIDE = (ES == 4);
+        // fp32 rows are wide: K is read from LDS per MFMA instead of held in
+        // registers, and relative rows are fetched one block at a time
         const unsigned char* k_lds = Ks + ((kb * 32 + li) * C::KPITCH + lh * C::HALF) * ES;
-        uint4 kf[WIDE ? 1 : NU];
-        if constexpr (!WIDE) lds_half_row<NU>(kf, k_lds);
-        auto kchain = [&](const uint4 (&b)[NU], f32x16_t acc) {
-          if constexpr (WIDE) return mma_chain_lds<T, NU, NC>(k_lds, b, acc);
-          else return mma_chain<T, NU, NC>(kf, b, acc);
-        };
-
-        if constexpr (PIPE) {
-          // F[jh][v] = k_(j0+32kb+jh) . qr[T(vmin + v)], v over BM+31 distances
-          if (p2c_mode == TERM_BAND) {
-#pragma unroll
-            for (int x = 0; x < FB; ++x) {
-              const int vb = wave + NW * x;
-              if (vb < C::NBV) {
-                const f32x16_t f = kchain(rowF[x], f32x16_t{});
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                  Fw[(rr_of(r) + 4 * lh) * C::FWP + vb * 32 + li] = f[r];
-              }
-            }
-          }
-          // E[u][i] = kr[T(umin + u)] . q_i, u over the wave's 63 distances
-          if (c2p_mode == TERM_BAND) {
-#pragma unroll
-            for (int ub = 0; ub < 2; ++ub) {
-              const f32x16_t e = mma_chain<T, NU, NC>(rowE[ub], qf, f32x16_t{});
-#pragma unroll
-              for (int r = 0; r < 16; ++r) Eww[(ub * 32 + rr_of(r) + 4 * lh) * 32 + li] = e[r];
-            }
-          }
-          load_next_rows(t, kb, p2c_mode, c2p_mode);
-        }
-        if (!PIPE && p2c_mode == TERM_BAND) {
+        if (p2c_mode == TERM_BAND) {
           // F[jh][v] = k_(j0+32kb+jh) . qr[T(vmin + v)], v over BM+31 distances
           const int vmin = (j0 + 32 * kb) - (i0 + BM - 1);
-          constexpr int FL = WIDE ? 1 : FB;             // blocks loaded together
 #pragma unroll
-          for (int t0 = 0; t0 < FB; t0 += FL) {
-            uint4 rf[FL][NU];
+          for (int x = 0; x < FB; ++x) {
+            const int vb = wave + NW * x;
+            if (vb < C::NBV) {
+              uint4 rf[NU];
+              load_half_row<NU>(rf, qr_lane + rel_off(vmin + vb * 32 + li, twok));
+              const f32x16_t f = mma_chain_lds<T, NU, NC>(k_lds, rf, f32x16_t{});
 #pragma unroll
-            for (int t = 0; t < FL; ++t) {
-              const int vb = wave + NW * (t0 + t);
-              if (vb < C::NBV)
-                load_half_row<NU>(rf[t], QRg + ((int64_t)rel_row(vmin + vb * 32 + li, twok) * p.ld_rel +
-                                                hoff + lh * C::HALF) * ES);
-            }
-#pragma unroll
-            for (int t = 0; t < FL; ++t) {
-              const int vb = wave + NW * (t0 + t);
-              if (vb < C::NBV) {
-                const f32x16_t f = kchain(rf[t], f32x16_t{});
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                  Fw[(rr_of(r) + 4 * lh) * C::FWP + vb * 32 + li] = f[r];
-              }
+              for (int r = 0; r < 16; ++r)
+                Fw[(rr_of(r) + 4 * lh) * C::FWP + vb * 32 + li] = f[r];
             }
           }
         }
-        if (!PIPE && c2p_mode == TERM_BAND) {
+        if (c2p_mode == TERM_BAND) {
           // E[u][i] = kr[T(umin + u)] . q_i, u over the wave's 63 distances
           const int umin = i0w - (j0 + 32 * kb + 31);
-          constexpr int EL = WIDE ? 1 : 2;              // blocks loaded together
 #pragma unroll
-          for (int u0 = 0; u0 < 2; u0 += EL) {
-            uint4 rf[EL][NU];
+          for (int ub = 0; ub < 2; ++ub) {
+            uint4 rf[NU];
+            load_half_row<NU>(rf, kr_lane + rel_off(umin + ub * 32 + li, twok));
+            const f32x16_t e = mma_chain<T, NU, NC>(rf, qf, f32x16_t{});
 #pragma unroll
-            for (int ub = 0; ub < EL; ++ub)
-              load_half_row<NU>(rf[ub], KRg + ((int64_t)rel_row(umin + (u0 + ub) * 32 + li, twok) *
-                                                   p.ld_rel + hoff + lh * C::HALF) * ES);
-#pragma unroll
-            for (int ub = 0; ub < EL; ++ub) {
-              const f32x16_t e = mma_chain<T, NU, NC>(rf[ub], qf, f32x16_t{});
-#pragma unroll
-              for (int r = 0; r < 16; ++r)
-                Eww[((u0 + ub) * 32 + rr_of(r) + 4 * lh) * 32 + li] = e[r];
-            }
+            for (int r = 0; r < 16; ++r) Eww[(ub * 32 + rr_of(r) + 4 * lh) * 32 + li] = e[r];
           }
         }
         if (p2c_mode == TERM_BAND) __syncthreads();  // F complete
 
         f32x16_t acc = (p2c_mode == TERM_CONST) ? c_init(cbuf, kb) : f32x16_t{};
-        acc = kchain(qf, acc);
+        acc = mma_chain_lds<T, NU, NC>(k_lds, qf, acc);
         if (c2p_mode == TERM_BAND) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[r] += e_base[(27 - rr_of(r)) * 32];
@@ -1136,31 +1099,326 @@ void dattn_fwd_kernel(FwdParams p) {
   }
 
   };
-  if (tw_ok) phase1(std::true_type{});
-  else phase1(std::false_type{});
+  if constexpr (ES == 4) {
+    if (tw_ok) phase1(std::true_type{});
+    else phase1(std::false_type{});
+  }
 
-  // ---- phase 2 (16-bit types): far tiles through the LDS ring -------------
-  // Far tiles 0..FL-1 and FR..tm-1 are numbered n = 0, 1, ...; tile n lives
-  // in ring slot n % NSTAGE. Loads run three tiles ahead; c_j of tile n+1 is
-  // formed (by MFMA, 16 keys per wave) while tile n is computed; one barrier
-  // per tile publishes both.
   if constexpr (ES == 2) {
+    // ---- K/V slots filled by direct-to-LDS loads (16-bit types) -------------
+    // A slot holds a K tile and a V tile as dense [BN][D] rows. K rows are
+    // stored with an XOR swizzle of their 16-byte units (conflict-free MFMA
+    // operand reads); V rows as they are, read with the transposing LDS read
+    // into the V^T operand.
+    const uint32_t ring = (uint32_t)(size_t)(__attribute__((address_space(3))) unsigned char*)smem;
+    constexpr int DPW = C::DMA_PER_WAVE;
+    constexpr int ROWB = C::UPR * 16;   // bytes of one slot row
+    // source offsets of this wave's loads (unit order swizzled per row)
+    uint32_t kdo[DPW], vdo[DPW];
+#pragma unroll
+    for (int x = 0; x < DPW; ++x) {
+      const int u_lds = 64 * (wave * DPW + x) + lane;
+      const int r = u_lds / C::UPR, pu = u_lds % C::UPR;
+      kdo[x] = (uint32_t)((r * p.ld_k + hoff) * ES + 16 * (pu ^ C::swz_k(r)));
+      vdo[x] = (uint32_t)((r * p.ld_v + hoff) * ES + 16 * (pu ^ C::swz_v(r)));
+    }
+    // load key tile t into the slot at LDS byte address slot_addr
+    auto issue_tile = [&](int t, uint32_t slot_addr) {
+      const int64_t j0 = (int64_t)t * BN;
+      const unsigned char* kt = Kg + (base + j0) * p.ld_k * ES;
+      const unsigned char* vt = Vg + (base + j0) * p.ld_v * ES;
+      const uint32_t slot = slot_addr + 1024 * wave * DPW;
+      if (j0 + BN <= ext) {
+#pragma unroll
+        for (int x = 0; x < DPW; ++x) dma16(slot + 1024 * x, kt, kdo[x]);
+#pragma unroll
+        for (int x = 0; x < DPW; ++x) dma16(slot + C::KT_BYTES + 1024 * x, vt, vdo[x]);
+      } else {
+        // the sequence ends inside the tile: rows past its end repeat its
+        // last row (never read beyond it; those keys are masked)
+        const int last = ext - 1 - (int)j0;
+#pragma unroll
+        for (int x = 0; x < DPW; ++x) {
+          const int r = (64 * (wave * DPW + x) + lane) / C::UPR;
+          const int back = r > last ? r - last : 0;
+          dma16(slot + 1024 * x, kt, kdo[x] - (uint32_t)(back * p.ld_k * ES));
+        }
+#pragma unroll
+        for (int x = 0; x < DPW; ++x) {
+          const int r = (64 * (wave * DPW + x) + lane) / C::UPR;
+          const int back = r > last ? r - last : 0;
+          dma16(slot + C::KT_BYTES + 1024 * x, vt, vdo[x] - (uint32_t)(back * p.ld_v * ES));
+        }
+      }
+    };
+
+    // B operand of the c_j products (16x16x32 MFMA): column 0 is qr[top
+    // row], column 1 qr[bottom row], the other columns zero
+    typename Ty<T>::frag cq[D / 32];
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m) {
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if ((lane & 15) < 2)
+        x = ld16(Rrows + ((lane & 15) * D + 32 * m + 8 * (lane >> 4)) * ES);
+      cq[m] = __builtin_bit_cast(typename Ty<T>::frag, x);
+    }
+    // c_j = k_j . qr[row] (which: 0 top, 1 bottom) of the 16 keys
+    // 16g .. 16g+15 of a slot's K tile, stored at cdst[16g ..]
+    auto c_group = [&](const unsigned char* ks, int g, int which, float* cdst) {
+      const int r = 16 * g + (lane & 15);
+      f32x4_t acc = f32x4_t{};
+#pragma unroll
+      for (int m = 0; m < D / 32; ++m) {
+        const int u = 4 * m + (lane >> 4);
+        const auto a = __builtin_bit_cast(typename Ty<T>::frag,
+                                          ld16(ks + r * ROWB + 16 * (u ^ C::swz_k(r))));
+        acc = Ty<T>::mma16(a, cq[m], acc);
+      }
+      // lane l holds column l % 16 and keys 16g + 4*(l/16) + 0..3
+      if ((lane & 15) == which)
+        *reinterpret_cast<f32x4_t*>(cdst + 16 * g + 4 * (lane >> 4)) = acc;
+    };
+
+    // per-lane operand offsets inside a slot
+    uint32_t kro[NU];   // K rows li (+32 kb), units lh*NU + x
+#pragma unroll
+    for (int x = 0; x < NU; ++x) kro[x] = li * ROWB + 16 * ((lh * NU + x) ^ C::swz_k(li));
+    const int vg = lane >> 4, vt4 = lane & 15;
+    const int vkey = 4 * (vg >> 1) + (vt4 >> 2);   // + 32 kb + 16 c + 8 h
+    uint32_t vro[C::NDB];
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+      const int u = 4 * db + 2 * (vg & 1) + ((vt4 & 3) >> 1);
+      vro[db] = vkey * ROWB + 16 * (u ^ C::swz_v(vkey)) + 8 * (vt4 & 1);
+    }
+    // V^T operand of the P.V MFMA from the V tile at vs
+    auto vop_slot = [&](const unsigned char* vs) {
+      return [=](int kb, int c, int db) {
+        const unsigned char* a0 = vs + vro[db] + (32 * kb + 16 * c) * ROWB;
+        const uint2 lo = lds_tr16(a0), hi = lds_tr16(a0 + 8 * ROWB);
+        return __builtin_bit_cast(typename Ty<T>::frag, make_uint4(lo.x, lo.y, hi.x, hi.y));
+      };
+    };
+    // this lane's K operand (key li of block kb) from the K tile at ks
+    auto k_operand = [&](const unsigned char* ks, int kb, uint4 (&kf)[NU]) {
+#pragma unroll
+      for (int x = 0; x < NU; ++x) kf[x] = ld16(ks + kro[x] + kb * 32 * ROWB);
+    };
+
+    // ---- phase 1 (16-bit types): general tiles ------------------------------
+    // Tiles with band terms or masked keys. Tile t sits in slot t's parity;
+    // the next general tile is loaded while it is computed. Every band
+    // product is wave-private: per 32-key half, E[u][i] = kr[T(u)] . q_i over
+    // the 63 distances u = i - j of the wave's queries and F[j][v] =
+    // k_j . qr[T(v)] over the 63 distances v = j - i are formed by MFMA
+    // (table rows gathered into the operands), stored in the wave's LDS
+    // scratch and read back along the diagonal, so no wave waits for another
+    // within a tile. A term that is saturated over all of a wave's pairs
+    // takes the constant path (a_i, or c_j from the wave's own small MFMAs).
+    // One barrier per tile, two when the tile holds masked keys.
+    auto phase1g = [&](auto twok) {
+      float* scr = reinterpret_cast<float*>(smem + C::OFF_SCR + wave * C::SCR_BYTES);
+      float* cjw = reinterpret_cast<float*>(smem + C::OFF_CJW + wave * BN * 4);
+      const float* e_rd = scr + (li + 4 - 4 * lh) * 32 + li;   // + (27 - rr) * 32
+      const float* f_rd = scr + 4 * lh * 65 + 31 - li;         // + rr * 65
+      struct Modes { int c2p, p2c, which; float a_off; };
+      // paths of the two terms over this wave's pairs with tile t
+      auto wave_modes = [&](int t) {
+        Modes m;
+        m.c2p = TERM_OFF;
+        m.p2c = TERM_OFF;
+        m.which = 0;
+        m.a_off = 0.f;
+        if (w_qlo > w_qhi) return m;   // no query of this wave exists
+        const int k_lo = t * BN, k_hi = min(t * BN + BN, ext) - 1;
+        if (has_p2c) {
+          if (k_lo - w_qhi >= sat_top) { m.p2c = TERM_CONST; m.which = 0; }
+          else if (k_hi - w_qlo <= sat_bot) { m.p2c = TERM_CONST; m.which = 1; }
+          else m.p2c = TERM_BAND;
+        }
+        if (has_c2p) {
+          if (w_qlo - k_hi >= sat_top) { m.c2p = TERM_CONST; m.a_off = a_top; }
+          else if (w_qhi - k_lo <= sat_bot) { m.c2p = TERM_CONST; m.a_off = a_bot; }
+          else m.c2p = TERM_BAND;
+        }
+        return m;
+      };
+      // one value per wave: branches on it stay scalar
+      auto uniform = [](Modes m) {
+        m.c2p = __builtin_amdgcn_readfirstlane(m.c2p);
+        m.p2c = __builtin_amdgcn_readfirstlane(m.p2c);
+        m.which = __builtin_amdgcn_readfirstlane(m.which);
+        return m;
+      };
+      // Table rows of the band operands: for half kb of tile t, E block ub
+      // covers the distances u = umin + 32 ub + 0..31 and F block vb the
+      // distances v = vmin + 32 vb + 0..31; lane li fetches row li of a block.
+      // The second half of a tile shares one block with the first: its E
+      // block 1 is the first half's E block 0 (same rows and queries, so the
+      // product is kept, not recomputed) and its F block 0 uses the first
+      // half's F block-1 rows. Two register blocks hold the rows in turn,
+      // each refetched as soon as a product has read it.
+      const unsigned char* krb = KRg + hoff * ES;   // this head's columns
+      const unsigned char* qrb = QRg + hoff * ES;
+      const uint32_t lhb = (uint32_t)(lh * C::HALF * ES);
+      uint4 rw[2][NU];
+      auto load_e = [&](int t, int kb, int ub, uint4 (&dst)[NU]) {
+        const int umin = i0w - (t * BN + 32 * kb + 31);
+        load_half_row<NU>(dst, krb + (rel_off(umin + 32 * ub + li, twok) + lhb));
+      };
+      auto load_f = [&](int t, int kb, int vb, uint4 (&dst)[NU]) {
+        const int vmin = (t * BN + 32 * kb) - (i0w + 31);
+        load_half_row<NU>(dst, qrb + (rel_off(vmin + 32 * vb + li, twok) + lhb));
+      };
+      // the rows the first half of tile t starts with (modes m)
+      auto load_first = [&](int t, const Modes& m) {
+        if (m.c2p == TERM_BAND) { load_e(t, 0, 0, rw[0]); load_e(t, 0, 1, rw[1]); }
+        else if (m.p2c == TERM_BAND) { load_f(t, 0, 0, rw[0]); load_f(t, 0, 1, rw[1]); }
+      };
+      // E[u][i] (two 32-distance blocks) into the scratch, then added along
+      // the diagonal; likewise F[j][v]. The scratch is rewritten only after
+      // this wave's own reads of it: LDS serves one wave's accesses in order.
+      auto add_e = [&](const f32x16_t& e0, const f32x16_t& e1, f32x16_t& acc) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) scr[(rr_of(r) + 4 * lh) * 32 + li] = e0[r];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) scr[(32 + rr_of(r) + 4 * lh) * 32 + li] = e1[r];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] += e_rd[(27 - rr_of(r)) * 32];
+      };
+      auto add_f = [&](const f32x16_t& f0, const f32x16_t& f1, f32x16_t& acc) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) scr[(rr_of(r) + 4 * lh) * 64 + li] = f0[r];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) scr[(rr_of(r) + 4 * lh) * 64 + 32 + li] = f1[r];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] += f_rd[rr_of(r) * 65];
+      };
+
+      int t = first_general;
+      int par = 0;   // slot of tile t
+      issue_tile(t, ring);
+      Modes m = wave_modes(t);
+      load_first(t, uniform(m));
+      while (t >= 0) {
+        const int tn = next_general(t);
+        const int j0 = t * BN;
+        const bool need_mask = j0 + BN > key_end;
+        uint64_t kvalid = ~0ull;
+        if (need_mask) {
+          const int j = j0 + lane;
+          bool ok = j < ext;
+          if (!VARLEN && mrow && ok && j >= first_bad) ok = mrow[j] != 0;
+          kvalid = (uint64_t)__ballot(ok);
+        }
+        wait_vm<0>();
+        __syncthreads();  // tile t in its slot; the other slot is free
+        const unsigned char* ks = smem + par * C::SLOT_BYTES;
+        const unsigned char* vs = ks + C::KT_BYTES;
+        if (kvalid != ~0ull) {
+          // masked or missing keys: zero their V rows (their scores are -inf)
+          for (int x = tid; x < BN * C::UPR; x += NT) {
+            const int r = x / C::UPR;
+            if (!((kvalid >> r) & 1ull))
+              *reinterpret_cast<uint4*>(const_cast<unsigned char*>(vs) + 16 * x) = make_uint4(0, 0, 0, 0);
+          }
+          __syncthreads();
+        }
+        m = uniform(m);
+        const Modes mn = uniform(tn >= 0 ? wave_modes(tn) : Modes{TERM_OFF, TERM_OFF, 0, 0.f});
+        if (m.p2c == TERM_CONST) {
+#pragma unroll
+          for (int g = 0; g < BN / 16; ++g) c_group(ks, g, m.which, cjw);
+        }
+        const bool eb = m.c2p == TERM_BAND, fb = m.p2c == TERM_BAND;
+        auto next_first = [&] { if (tn >= 0) load_first(tn, mn); };
+        auto q_k = [&](int kb, const uint4 (&kf)[NU]) {
+          const f32x16_t c = (m.p2c == TERM_CONST) ? c_init(cjw, kb) : f32x16_t{};
+          return mma_chain<T, NU, NC>(kf, qf, c);
+        };
+        auto mask_keys = [&](int kb, f32x16_t& acc) {
+          if (kvalid != ~0ull) {
+            const uint32_t kv = (uint32_t)(kvalid >> (kb * 32 + 4 * lh));   // this lane's keys
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (!((kv >> rr_of(r)) & 1u)) acc[r] = NEG_INF;
+          }
+        };
+        f32x16_t s[2];
+        static_assert(C::NKB == 2, "two key halves per tile");
+        // ---- first half: rows E(0,0), E(0,1) then F(0,0), F(0,1) ---------
+        f32x16_t e_keep;
+        {
+          uint4 kf[NU];
+          k_operand(ks, 0, kf);
+          f32x16_t acc = q_k(0, kf);
+          if (eb) {
+            const f32x16_t e0 = mma_chain<T, NU, NC>(rw[0], qf, f32x16_t{});
+            const f32x16_t e1 = mma_chain<T, NU, NC>(rw[1], qf, f32x16_t{});
+            e_keep = e0;   // the second half's E block 1
+            if (fb) { load_f(t, 0, 0, rw[0]); load_f(t, 0, 1, rw[1]); }
+            else load_e(t, 1, 0, rw[0]);
+            add_e(e0, e1, acc);
+          }
+          if (fb) {
+            const f32x16_t f0 = mma_chain<T, NU, NC>(kf, rw[0], f32x16_t{});
+            if (eb) load_e(t, 1, 0, rw[0]);
+            else load_f(t, 1, 1, rw[0]);
+            // rw[1] stays: its rows are the second half's F block 0
+            const f32x16_t f1 = mma_chain<T, NU, NC>(kf, rw[1], f32x16_t{});
+            add_f(f0, f1, acc);
+          }
+          mask_keys(0, acc);
+          s[0] = acc;
+        }
+        // ---- second half: rows E(1,0) (E(1,1) kept), then F(1,1) ----------
+        {
+          uint4 kf[NU];
+          k_operand(ks, 1, kf);
+          f32x16_t acc = q_k(1, kf);
+          if (eb) {
+            const f32x16_t e0 = mma_chain<T, NU, NC>(rw[0], qf, f32x16_t{});
+            if (fb) load_f(t, 1, 1, rw[0]);
+            else next_first();
+            add_e(e0, e_keep, acc);
+          }
+          if (fb) {
+            const f32x16_t f0 = mma_chain<T, NU, NC>(kf, rw[1], f32x16_t{});
+            const f32x16_t f1 = mma_chain<T, NU, NC>(kf, rw[0], f32x16_t{});
+            next_first();
+            add_f(f0, f1, acc);
+          }
+          if (!eb && !fb) next_first();
+          // the next general tile's K and V, after every row fetch this tile
+          // consumes (a wait for those rows then never waits for these loads)
+          if (tn >= 0) issue_tile(tn, ring + (par ^ 1) * C::SLOT_BYTES);
+          mask_keys(1, acc);
+          s[1] = acc;
+        }
+        softmax_pv(s, m.a_off, vop_slot(vs));
+        t = tn;
+        m = mn;
+        par ^= 1;
+      }
+      wait_vm<0>();
+      __syncthreads();  // slots and scratch free for the far tiles
+    };
+    if (first_general >= 0) {
+      if (tw_ok) phase1g(std::true_type{});
+      else phase1g(std::false_type{});
+    }
+
+    // ---- phase 2 (16-bit types): far tiles through the LDS ring -----------
+    // Far tiles 0..FL-1 and FR..tm-1 are numbered n = 0, 1, ...; tile n lives
+    // in ring slot n % NSTAGE. Loads run three tiles ahead; c_j of tile n+1 is
+    // formed (by MFMA, 16 keys per wave) while tile n is computed; one barrier
+    // per tile publishes both.
     const int nfar = FL + max(tm - FR, 0);
     if (nfar > 0) {
       auto far_tile = [&](int n) { return n < FL ? n : FR + (n - FL); };
-      const uint32_t ring = (uint32_t)(size_t)(__attribute__((address_space(3))) unsigned char*)smem;
-      constexpr int DPW = C::DMA_PER_WAVE;
-      constexpr int NDMA = 2 * DPW;   // loads of one tile issued by one wave
-      constexpr int ROWB = C::UPR * 16;   // bytes of one ring row
-      // source offsets of this wave's loads (unit order swizzled per row)
-      uint32_t kdo[DPW], vdo[DPW];
-#pragma unroll
-      for (int x = 0; x < DPW; ++x) {
-        const int u_lds = 64 * (wave * DPW + x) + lane;
-        const int r = u_lds / C::UPR, pu = u_lds % C::UPR;
-        kdo[x] = (uint32_t)((r * p.ld_k + hoff) * ES + 16 * (pu ^ C::swz_k(r)));
-        vdo[x] = (uint32_t)((r * p.ld_v + hoff) * ES + 16 * (pu ^ C::swz_v(r)));
-      }
+      // tile n in ring slot n % NSTAGE: its K tile, then its V tile
+      auto kslot = [&](int n) { return smem + (n % C::NSTAGE) * C::SLOT_BYTES; };
+      auto vslot = [&](int n) { return kslot(n) + C::KT_BYTES; };
       auto issue = [&](int n) {
         const int64_t j0 = far_tile(n) * BN;
         const unsigned char* kt = Kg + (base + j0) * p.ld_k * ES;
@@ -1171,68 +1429,23 @@ void dattn_fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int x = 0; x < DPW; ++x) dma16(slot + C::KT_BYTES + 1024 * x, vt, vdo[x]);
       };
-      // wait for every tile but the newest k issued ones
-      auto wait_all_but = [&](int k) {
-        if (k <= 0) wait_vm<0>();
-        else if (k == 1) wait_vm<NDMA>();
-        else wait_vm<2 * NDMA>();
-      };
-
-      // c_j of a ring tile: keys 16*wave.. by the 16x16x32 MFMA against a B
-      // operand whose column 0 is qr[top row] and column 1 qr[bottom row]
-      typename Ty<T>::frag cq[D / 32];
-#pragma unroll
-      for (int m = 0; m < D / 32; ++m) {
-        uint4 x = make_uint4(0, 0, 0, 0);
-        if ((lane & 15) < 2)
-          x = ld16(Rrows + ((lane & 15) * D + 32 * m + 8 * (lane >> 4)) * ES);
-        cq[m] = __builtin_bit_cast(typename Ty<T>::frag, x);
-      }
       auto compute_c = [&](int n) {
-        const int which = far_tile(n) < FL ? 1 : 0;
-        const unsigned char* ks = smem + (n % C::NSTAGE) * C::SLOT_BYTES;
-        const int r = 16 * wave + (lane & 15);
-        f32x4_t acc = f32x4_t{};
-#pragma unroll
-        for (int m = 0; m < D / 32; ++m) {
-          const int u = 4 * m + (lane >> 4);
-          const auto a = __builtin_bit_cast(typename Ty<T>::frag,
-                                            ld16(ks + r * ROWB + 16 * (u ^ C::swz_k(r))));
-          acc = Ty<T>::mma16(a, cq[m], acc);
-        }
-        // lane l holds column l % 16 and keys 16*wave + 4*(l/16) + 0..3
-        if ((lane & 15) == which)
-          *reinterpret_cast<f32x4_t*>(cring + (n % 3) * BN + 16 * wave + 4 * (lane >> 4)) = acc;
+        c_group(kslot(n), wave, far_tile(n) < FL ? 1 : 0, cring + (n % 3) * BN);
       };
-
-      // per-lane operand offsets inside a slot
-      uint32_t kro[NU];   // K rows li (+32 kb), units lh*NU + x
-#pragma unroll
-      for (int x = 0; x < NU; ++x) kro[x] = li * ROWB + 16 * ((lh * NU + x) ^ C::swz_k(li));
-      const int vg = lane >> 4, vt4 = lane & 15;
-      const int vkey = 4 * (vg >> 1) + (vt4 >> 2);   // + 32 kb + 16 c + 8 h
-      uint32_t vro[C::NDB];
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db) {
-        const int u = 4 * db + 2 * (vg & 1) + ((vt4 & 3) >> 1);
-        vro[db] = vkey * ROWB + 16 * (u ^ C::swz_v(vkey)) + 8 * (vt4 & 1);
-      }
 
       // The loop is instantiated with and without the P2C term. It is
       // software-pipelined: the scores of tile n+1 are produced by MFMAs
-      // issued inside tile n's softmax, after its rescale decision, so they
-      // overlap its exponentials; c_j runs two tiles ahead so that those
-      // scores never wait for another wave.
+      // issued in the same block as tile n's exponentials; c_j runs two
+      // tiles ahead so that those scores never wait for another wave.
       auto ring_loop = [&](auto pc) {
         constexpr bool PC = decltype(pc)::value;
         auto scores = [&](int n, f32x16_t (&s)[C::NKB]) {
-          const unsigned char* ks = smem + (n % C::NSTAGE) * C::SLOT_BYTES;
+          const unsigned char* ks = kslot(n);
           const float* cb = cring + (n % 3) * BN;
 #pragma unroll
           for (int kb = 0; kb < C::NKB; ++kb) {
             uint4 kf[NU];
-#pragma unroll
-            for (int x = 0; x < NU; ++x) kf[x] = ld16(ks + kro[x] + kb * 32 * ROWB);
+            k_operand(ks, kb, kf);
             f32x16_t acc = f32x16_t{};
             if constexpr (PC) acc = c_init(cb, kb);
             s[kb] = mma_chain<T, NU, NC>(kf, qf, acc);
@@ -1242,20 +1455,14 @@ void dattn_fwd_kernel(FwdParams p) {
         auto step = [&](int n, f32x16_t (&s_cur)[C::NKB], f32x16_t (&s_nxt)[C::NKB]) {
           if (n + C::NSTAGE - 1 < nfar) issue(n + C::NSTAGE - 1);   // into the slot of tile n-1
           if (PC && n + 2 < nfar) compute_c(n + 2);
-          const int t = far_tile(n);
-          const float a_off = has_c2p ? (t < FL ? a_top : a_bot) : 0.f;
-          const unsigned char* vs = smem + (n % C::NSTAGE) * C::SLOT_BYTES + C::KT_BYTES;
+          const float a_off = has_c2p ? (far_tile(n) < FL ? a_top : a_bot) : 0.f;
           softmax_pv_mid(
-              s_cur, a_off,
-              [&](int kb, int c, int db) {
-                const unsigned char* a0 = vs + vro[db] + (32 * kb + 16 * c) * ROWB;
-                const uint2 lo = lds_tr16(a0), hi = lds_tr16(a0 + 8 * ROWB);
-                return __builtin_bit_cast(typename Ty<T>::frag, make_uint4(lo.x, lo.y, hi.x, hi.y));
-              },
+              s_cur, a_off, vop_slot(vslot(n)),
               // unconditional, so the MFMAs share a block with the
               // exponentials; after the last tile they read a stale slot
               // and their result is not used
-              [&] { scores(n + 1, s_nxt); });
+              [&] { scores(n + 1, s_nxt); },
+              [&](f32x16_t (&sr)[C::NKB]) { scores(n, sr); });
           // all of this wave's loads done: tile n+3 (and c_j of n+2) are
           // visible after the barrier, and the slot of tile n is free
           wait_vm<0>();

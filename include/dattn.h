@@ -108,7 +108,8 @@ int rel_bucket(int32_t* rel_idx, int32_t max_len, int32_t position_buckets,
  * Errors: INVALID_ARGUMENT (null pointer, B < 0, L < 0, H < 1, ld < H*d,
  * rel_max_len < L or n_rel < 1 when flags != 0, unknown flag bits, NaN
  * scale); UNSUPPORTED (d not 32/64/128, unknown dtype, L > 8192,
- * misaligned pointer or stride); HIP_ERROR. B*L == 0 is a no-op.
+ * misaligned pointer or stride, relative tables of n_rel * ld_rel elements
+ * spanning more than 2^31 - 1 bytes); HIP_ERROR. B*L == 0 is a no-op.
  */
 int dattn_fwd_padded(const void* q, const void* k, const void* v,
                      int64_t ld_q, int64_t ld_k, int64_t ld_v,

@@ -81,6 +81,8 @@ def varlen(**kw):
     (dict(d=48), UNS), (dict(d=256), UNS), (dict(dtype=3), UNS), (dict(L=8193, rel_max_len=9000), UNS),
     (dict(q=MIS), UNS), (dict(out=MIS), UNS), (dict(ld_q=772), UNS), (dict(qr=MIS), UNS),
     (dict(dtype=0, ld_q=770), UNS),
+    # relative tables whose row offsets would not fit in 31 bits
+    (dict(n_rel=1 << 20, ld_rel=1 << 10), UNS), (dict(n_rel=1 << 20, ld_rel=1 << 10, flags=1), UNS),
 ])
 def test_padded_rejections(kw, status):
     assert padded(**kw) == status
@@ -101,7 +103,7 @@ def test_flags0_needs_no_relative_tables():
 @pytest.mark.parametrize("kw,status", [
     (dict(cu=None), INV), (dict(nseq=-1), INV), (dict(total=-1), INV), (dict(max_seqlen=-1), INV),
     (dict(rel_max_len=100), INV), (dict(max_seqlen=9000, rel_max_len=9000), UNS), (dict(q=None), INV),
-    (dict(d=16), UNS), (dict(k=MIS), UNS),
+    (dict(d=16), UNS), (dict(k=MIS), UNS), (dict(n_rel=1 << 20, ld_rel=1 << 10), UNS),
 ])
 def test_varlen_rejections(kw, status):
     assert varlen(**kw) == status
