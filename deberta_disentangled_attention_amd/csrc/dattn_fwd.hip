@@ -408,7 +408,7 @@ void dattn_fwd_kernel(FwdParams p) {
   float* cring = reinterpret_cast<float*>(smem + C::OFF_CR);
   unsigned char* Rrows = smem + C::OFF_R;   // qr_top, qr_bot, kr_top, kr_bot
   int* misc = reinterpret_cast<int*>(smem + C::OFF_MISC);
-  uint32_t* Tw = reinterpret_cast<uint32_t*>(smem + C::OFF_TW);   // row offsets, sat_bot <= d <= sat_top
+  uint32_t* Tw = reinterpret_cast<uint32_t*>(smem + C::OFF_TW);   // row offsets of a window of distances
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -518,17 +518,17 @@ void dattn_fwd_kernel(FwdParams p) {
   auto row_off = [&](int r) { return (uint32_t)clamp_row(r) * ld_rel_b; };
   int sat_top = 1 << 30, sat_bot = -(1 << 30);
   int row_hi = 0, row_lo = 0;
-  int wlen = 0;
+  int tw0 = 0, tw_n = 1;   // staged window: distances tw0 .. tw0 + tw_n - 1
   bool tw_ok = false;
   // Byte offset of the qr / kr row of a signed distance. The table is
-  // staged in LDS as offsets for the distances sat_bot .. sat_top (the
-  // end entries stand for everything beyond), or read from global memory
-  // when that window is too long; the two cases are separate instantiations
-  // of the general-tile loops, so the common one never waits on a global
-  // load.
+  // staged in LDS as offsets for a window of distances that contains
+  // sat_bot .. sat_top (its end entries stand for everything beyond), or
+  // read from global memory when that window is too long; the two cases
+  // are separate instantiations of the general-tile loops, so the common
+  // one never waits on a global load.
   auto rel_off = [&](int dist, auto twok) -> uint32_t {
     if constexpr (decltype(twok)::value) {
-      return Tw[min(max(dist - sat_bot, 0), wlen + 1)];
+      return Tw[min(max(dist - tw0, 0), tw_n - 1)];
     } else {
       int r;
       if (dist <= sat_bot) r = row_lo;
@@ -542,20 +542,55 @@ void dattn_fwd_kernel(FwdParams p) {
     }
   };
   if (has_c2p || has_p2c) {
+    // The table is non-decreasing, so both thresholds (the first index that
+    // holds its last value, the first that leaves its first value) are found
+    // in two rounds: NT samples spaced `step` apart (the last one at n-1)
+    // bracket them, then one thread per bracket entry settles each. The
+    // window staged in LDS is the union of the two brackets and everything
+    // between them: its end entries are saturated, so clamping an index
+    // into it reproduces the table beyond the thresholds.
     const int32_t* tb = p.rel_idx;
+    const int step = tbl_n > 1 ? (tbl_n - 2) / (NT - 1) + 1 : 1;
+    if (tid == 0) { misc[2] = NT; misc[3] = NT; misc[4] = tbl_n; misc[5] = tbl_n; }
     row_hi = tb[tbl_n - 1];
     row_lo = tb[0];
-    const int first_top = block_first_true<NT>(tbl_n, [&](int x) { return tb[x] == row_hi; },
-                                               &misc[2], tid);
-    const int first_above_bot = block_first_true<NT>(
-        tbl_n, [&](int x) { return tb[x] != row_lo; }, &misc[2], tid);
+    const int xs = min(tid * step, tbl_n - 1);
+    const int vs = tb[xs];
+    __syncthreads();
+    if (vs == row_hi) atomicMin(&misc[2], tid);
+    if (vs != row_lo) atomicMin(&misc[3], tid);
+    __syncthreads();
+    const int t_top = misc[2], t_bot = misc[3];   // t_top <= NT-1: the last sample is n-1
+    // brackets: first_top in (lo_top, hi_top], first_above_bot in (lo_bot, hi_bot]
+    const int hi_top = min(t_top * step, tbl_n - 1);
+    const int lo_top = t_top > 0 ? min((t_top - 1) * step, tbl_n - 1) : -1;
+    const bool flat = t_bot >= NT;                  // every entry equals the first
+    const int hi_bot = flat ? tbl_n : min(t_bot * step, tbl_n - 1);
+    const int lo_bot = flat ? tbl_n - 1 : (t_bot > 0 ? min((t_bot - 1) * step, tbl_n - 1) : -1);
+    // half of the threads search each bracket (at most `step` entries)
+    if (tid < NT / 2) {
+      for (int k = tid; k < step; k += NT / 2) {
+        const int x = lo_top + 1 + k;
+        if (x < hi_top && tb[x] == row_hi) atomicMin(&misc[4], x);
+      }
+    } else if (!flat) {
+      for (int k = tid - NT / 2; k < step; k += NT / 2) {
+        const int x = lo_bot + 1 + k;
+        if (x < hi_bot && tb[x] != row_lo) atomicMin(&misc[5], x);
+      }
+    }
+    // window: table entries lo_bot .. hi_top (clamped into the table)
+    const int w0 = max(lo_bot, 0), w1 = max(hi_top, w0);
+    tw0 = w0 - (R - 1);
+    tw_n = w1 - w0 + 1;
+    tw_ok = !flat && tw_n <= C::TW;
+    if (tw_ok)
+      for (int x = tid; x < tw_n; x += NT) Tw[x] = row_off(tb[w0 + x]);
+    __syncthreads();
+    const int first_top = min(misc[4], hi_top);
+    const int first_above_bot = flat ? tbl_n : min(misc[5], hi_bot);
     sat_top = first_top - (R - 1);
     sat_bot = first_above_bot - 1 - (R - 1);
-    wlen = sat_top - sat_bot - 1;
-    tw_ok = wlen + 2 <= C::TW;
-    if (tw_ok)
-      for (int x = tid; x < wlen + 2; x += NT)
-        Tw[x] = row_off(x == 0 ? row_lo : (x == wlen + 1 ? row_hi : tb[sat_bot + x + R - 1]));
     // stage the two saturation rows of qr and kr (this head) in LDS
     constexpr int RU = D * ES / 16;
     for (int x = tid; x < 4 * RU; x += NT) {
