@@ -1488,6 +1488,12 @@ void dattn_fwd_kernel(FwdParams p) {
         };
         // tile n: scores in s_cur; produces the scores of tile n+1 in s_nxt
         auto step = [&](int n, f32x16_t (&s_cur)[C::NKB], f32x16_t (&s_nxt)[C::NKB]) {
+          // c_j of tile n+1 (formed in the previous step) goes into s_nxt
+          // first, so its LDS reads have the exponentials to land
+          if constexpr (PC) {
+#pragma unroll
+            for (int kb = 0; kb < C::NKB; ++kb) s_nxt[kb] = c_init(cring + ((n + 1) % 3) * BN, kb);
+          }
           if (n + C::NSTAGE - 1 < nfar) issue(n + C::NSTAGE - 1);   // into the slot of tile n-1
           if (PC && n + 2 < nfar) compute_c(n + 2);
           const float a_off = has_c2p ? (far_tile(n) < FL ? a_top : a_bot) : 0.f;
@@ -1496,7 +1502,15 @@ void dattn_fwd_kernel(FwdParams p) {
               // unconditional, so the MFMAs share a block with the
               // exponentials; after the last tile they read a stale slot
               // and their result is not used
-              [&] { scores(n + 1, s_nxt); },
+              [&] {
+                const unsigned char* ks = kslot(n + 1);
+#pragma unroll
+                for (int kb = 0; kb < C::NKB; ++kb) {
+                  uint4 kf[NU];
+                  k_operand(ks, kb, kf);
+                  s_nxt[kb] = mma_chain<T, NU, NC>(kf, qf, PC ? s_nxt[kb] : f32x16_t{});
+                }
+              },
               [&](f32x16_t (&sr)[C::NKB]) { scores(n, sr); });
           // all of this wave's loads done: tile n+3 (and c_j of n+2) are
           // visible after the barrier, and the slot of tile n is free
