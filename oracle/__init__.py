@@ -10,16 +10,18 @@ the method's arithmetic.
 Modules:
   bucket    - relative-position bucket and row table, exact integers
   attention - scores, masked softmax and output per (sequence, head)
+  pack      - padded <-> packed rows and their metadata
 
-Pins (tests marked "not gpu") tie both modules to things other than
+Pins (tests marked "not gpu") tie the modules to things other than
 themselves: exact integer identities and invariants of the bucket, a
 pure-Python brute force on tiny inputs, special cases that reduce to
 torch's scaled_dot_product_attention, index-revealing inputs that expose
 which table row each score term reads, a hand-derived worked example
-under tests/golden/, and mask / packing invariants.
+under tests/golden/, mask / packing invariants, and packing examples
+worked by hand with a pure-Python brute force beside them.
 """
 
-from . import attention, bucket  # noqa: F401
+from . import attention, bucket, pack  # noqa: F401
 from .attention import (C2P, P2C, dattn_padded, dattn_rows, dattn_varlen,  # noqa: F401
                         default_scale)
 from .bucket import log_bucket, rel_index_table, span  # noqa: F401
