@@ -2,6 +2,7 @@
 """Benchmark of the disentangled-attention forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4]
+    python bench.py --pack [--workload c3]     # padded vs device-packed
 
 A step is one pass of the whole hot path over one batch of synthetic input:
 the relative-row table (rel_bucket) and the fused forward
@@ -15,6 +16,13 @@ valid (query, key) pair and head), tokens/s, the roofline object of the
 dominant kernel (the fused forward; its average duration from HIP events
 recorded on the launch stream around each launch) and the CPU oracle timed
 on a bounded sample of the same workload.
+
+--pack times, for a padded workload with a mask, the padded forward beside
+the packed route: dattn_pack_index on the mask, dattn_pack_rows of the
+fused QKV rows, the packed forward, and dattn_unpack_rows of the output.
+The metadata and the packed activations are built once per batch and reused
+by every layer, so the line reports the per-layer forward times and the
+per-batch packing cost separately.
 """
 
 from __future__ import annotations
@@ -193,6 +201,96 @@ def write_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
     print(json.dumps(rec))
 
 
+def _timed(fn, steps, warmup):
+    """Average ms of fn() from HIP events on torch's current stream (the
+    stream the binding launches on)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def bench_pack(args):
+    import numpy as np
+    import torch
+    import deberta_disentangled_attention_amd as dd
+
+    w = build_workload(args.workload)
+    if w.packed or w.mask is None:
+        raise SystemExit("--pack needs a padded workload with a mask (c2, c3)")
+    tdt = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(tdt).cuda()
+    hd = w.H * w.d
+    qkv = torch.cat([dev(w.q), dev(w.k), dev(w.v)], dim=-1)        # fused [B, L, 3*H*d]
+    qr, kr = dev(w.qr), dev(w.kr)
+    mask = torch.from_numpy(np.ascontiguousarray(w.mask, np.uint8)).cuda()
+    table = dd.rel_bucket(w.L, w.position_buckets, w.max_relative_positions, device="cuda")
+    out_pad = torch.empty((w.B, w.L, hd), dtype=tdt, device="cuda")
+    cu, tr, rp, mx = dd.pack_index(mask)
+    total, max_len = int(cu[-1].item()), int(mx.item())   # host metadata, read once per batch
+    packed = torch.empty((total, 3 * hd), dtype=tdt, device="cuda")
+    out_pk = torch.empty((total, hd), dtype=tdt, device="cuda")
+    back = torch.empty((w.B, w.L, hd), dtype=tdt, device="cuda")
+    q, k, v = qkv[..., :hd], qkv[..., hd:2 * hd], qkv[..., 2 * hd:]
+    pq, pk, pv = packed[:, :hd], packed[:, hd:2 * hd], packed[:, 2 * hd:]
+
+    def padded():
+        dd.dattn_fwd_padded(q, k, v, qr, kr, table, w.L, mask, w.H, w.d, flags=w.flags,
+                            out=out_pad)
+
+    def index():
+        dd.lib().dattn_pack_index(mask.data_ptr(), w.B, w.L, cu.data_ptr(), tr.data_ptr(),
+                                  rp.data_ptr(), mx.data_ptr(), dd._stream(mask))
+
+    def pack():
+        dd.pack_rows(qkv, tr, out=packed)
+
+    def attn():
+        dd.dattn_fwd_varlen(pq, pk, pv, qr, kr, table, w.L, cu, max_len, w.H, w.d,
+                            flags=w.flags, out=out_pk)
+
+    def unpack():
+        dd.unpack_rows(out_pk, rp, w.B, w.L, out=back)
+
+    S, W = args.steps, args.warmup
+    t_pad, t_idx, t_pack, t_attn, t_unpack = (_timed(f, S, W)
+                                              for f in (padded, index, pack, attn, unpack))
+    # the whole route once more, back to back, and a check that it agrees
+    t_route = _timed(lambda: (index(), pack(), attn(), unpack()), S, W)
+    same = bool(torch.equal(back, out_pad))
+    es = qkv.element_size()
+    pack_bytes = total * 3 * hd * es * 2 + w.B * w.L * 4
+    unpack_bytes = (total + w.B * w.L) * hd * es + w.B * w.L * 4
+    fixed = t_idx + t_pack + t_unpack
+    gain = t_pad - t_attn
+    res = {
+        "metric": "padded vs device-packed forward (ms)",
+        "workload": describe(w), "dtype": w.dtype, "nseq": w.B, "seq_len": w.L,
+        "total_tokens": total, "max_seqlen": max_len,
+        "padding_fraction": round(1.0 - total / (w.B * w.L), 4),
+        "steps": S, "warmup": W,
+        "padded_fwd_ms": round(t_pad, 4),
+        "packed_fwd_ms": round(t_attn, 4),
+        "pack_index_ms": round(t_idx, 4),
+        "pack_rows_qkv_ms": round(t_pack, 4),
+        "unpack_rows_ms": round(t_unpack, 4),
+        "packed_route_ms": round(t_route, 4),
+        "route_equals_padded": same,
+        "pack_rows_GBps": round(pack_bytes / (t_pack * 1e-3) / 1e9, 1),
+        "unpack_rows_GBps": round(unpack_bytes / (t_unpack * 1e-3) / 1e9, 1),
+        "layers_to_amortise_packing": (round(fixed / gain, 3) if gain > 0 else None),
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--write-traffic":
         write_traffic(*sys.argv[2:6])
@@ -209,6 +307,8 @@ def main():
     ap.add_argument("--cpu-units", type=int, default=16)
     ap.add_argument("--flags", type=int, default=None,
                     help="override the position terms (0 none, 1 C2P, 2 P2C, 3 both)")
+    ap.add_argument("--pack", action="store_true",
+                    help="padded forward vs the device-packed route on a padded workload")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -225,6 +325,11 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     dd.lib()
+    if args.pack:
+        if args.workload == "c4":
+            args.workload = "c3"
+        bench_pack(args)
+        return
     w = build_workload(args.workload)
     if args.flags is not None:
         w.flags = args.flags

@@ -52,6 +52,11 @@ def lib() -> ctypes.CDLL:
         h.dattn_fwd_varlen.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, i64, i32, vp, i32,
                                        vp, i32, i32, i64, vp, i32, i32, i32, u32, f32, vp]
         h.dattn_fwd_varlen.restype = ctypes.c_int
+        h.dattn_pack_index.argtypes = [vp, i32, i32, vp, vp, vp, vp, vp]
+        h.dattn_pack_index.restype = ctypes.c_int
+        for fn in (h.dattn_pack_rows, h.dattn_unpack_rows):
+            fn.argtypes = [vp, i64, i64, vp, i64, i64, vp, i64, vp]
+            fn.restype = ctypes.c_int
         h.dattn_strerror.argtypes = [ctypes.c_int]
         h.dattn_strerror.restype = ctypes.c_char_p
         _lib_handle = h
@@ -161,4 +166,83 @@ def dattn_fwd_varlen(q, k, v, qr, kr, rel_idx, rel_max_len: int, cu_seqlens, max
         int(max_seqlen), T, _ptr(out), H, d, _dtype_code(q), int(flags), float(scale),
         _stream(q))
     _check(st, "dattn_fwd_varlen")
+    return out
+
+
+def pack_index(mask, B: Optional[int] = None, L: Optional[int] = None, *, device=None):
+    """Packing metadata of a [B, L] mask (uint8/bool, or None for all valid,
+    then B and L are required): returns device int32 tensors (cu_seqlens
+    [B+1], token_rows [B*L], row_to_packed [B*L], max_seqlen [1])."""
+    import torch
+    if mask is not None:
+        if mask.dtype == torch.bool:
+            mask = mask.view(torch.uint8)
+        if mask.dtype != torch.uint8 or mask.dim() != 2 or not mask.is_contiguous():
+            raise ValueError("mask must be a contiguous [B, L] uint8/bool tensor")
+        B, L = mask.shape
+        device = mask.device
+    if B is None or L is None:
+        raise ValueError("B and L are required without a mask")
+    device = device if device is not None else "cuda"
+    i32 = dict(dtype=torch.int32, device=device)
+    cu = torch.empty(B + 1, **i32)
+    token_rows = torch.empty(B * L, **i32)
+    row_to_packed = torch.empty(B * L, **i32)
+    max_len = torch.empty(1, **i32)
+    st = lib().dattn_pack_index(_ptr(mask), int(B), int(L), _ptr(cu), _ptr(token_rows),
+                                _ptr(row_to_packed), _ptr(max_len), _stream(cu))
+    _check(st, "dattn_pack_index")
+    return cu, token_rows, row_to_packed, max_len
+
+
+def _rows2d(t, name: str):
+    """[..., W] with a contiguous last dimension and uniformly strided rows ->
+    (n_rows, row_bytes, row_stride_bytes)."""
+    if t.dim() < 2 or t.stride(-1) != 1:
+        raise ValueError(f"{name}: rows must have a contiguous last dimension")
+    ld = t.stride(-2)
+    expect = ld
+    for i in range(t.dim() - 3, -1, -1):
+        expect *= t.shape[i + 1]
+        if t.shape[i] > 1 and t.stride(i) != expect:
+            raise ValueError(f"{name}: rows must be uniformly strided")
+    n = t.numel() // t.shape[-1] if t.shape[-1] else 0
+    es = t.element_size()
+    return n, t.shape[-1] * es, ld * es
+
+
+def pack_rows(src, token_rows, total: Optional[int] = None, *, out=None):
+    """src [B, L, W] or [B*L, W] -> out [total, W] (out[r] = src[token_rows[r]]).
+    total defaults to B*L (rows past cu[B] are then left unwritten)."""
+    import torch
+    n_src, row_bytes, ld_src = _rows2d(src, "src")
+    W = src.shape[-1]
+    if out is None:
+        out = torch.empty((n_src if total is None else int(total), W), dtype=src.dtype,
+                          device=src.device)
+    if out.dtype != src.dtype or out.shape[-1] != W:
+        raise ValueError("out must match src in dtype and row width")
+    n_out, _, ld_dst = _rows2d(out, "out")
+    n_rows = min(token_rows.numel(), n_out)
+    st = lib().dattn_pack_rows(_ptr(src), ld_src, n_src, _ptr(token_rows), n_rows, row_bytes,
+                               _ptr(out), ld_dst, _stream(src))
+    _check(st, "dattn_pack_rows")
+    return out
+
+
+def unpack_rows(src, row_to_packed, B: int, L: int, *, out=None):
+    """src [T, W] packed rows -> out [B, L, W] with zero rows at the padding."""
+    import torch
+    n_src, row_bytes, ld_src = _rows2d(src, "src")
+    W = src.shape[-1]
+    if out is None:
+        out = torch.empty((B, L, W), dtype=src.dtype, device=src.device)
+    n_out, _, ld_dst = _rows2d(out, "out")
+    if n_out != B * L or out.dtype != src.dtype or out.shape[-1] != W:
+        raise ValueError("out must hold B*L rows of src's width and dtype")
+    if row_to_packed.numel() < B * L:
+        raise ValueError("row_to_packed must have B*L entries")
+    st = lib().dattn_unpack_rows(_ptr(src), ld_src, n_src, _ptr(row_to_packed), B * L, row_bytes,
+                                 _ptr(out), ld_dst, _stream(src))
+    _check(st, "dattn_unpack_rows")
     return out

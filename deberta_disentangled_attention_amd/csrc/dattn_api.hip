@@ -111,6 +111,45 @@ int dattn_fwd_varlen(const void* q, const void* k, const void* v, int64_t ld_q, 
   return dattn::launch_fwd(p, dtype, d, true, stream);
 }
 
+int dattn_pack_index(const uint8_t* mask, int32_t B, int32_t L, int32_t* cu_seqlens,
+                     int32_t* token_rows, int32_t* row_to_packed, int32_t* max_seqlen,
+                     hipStream_t stream) {
+  if (B < 0 || L < 0 || !cu_seqlens) return DATTN_ERR_INVALID_ARGUMENT;
+  const int64_t n = (int64_t)B * L;
+  if (n > INT32_MAX || B == INT32_MAX) return DATTN_ERR_UNSUPPORTED;  // int32 indices
+  if (n > 0 && (!token_rows || !row_to_packed)) return DATTN_ERR_INVALID_ARGUMENT;
+  return dattn::launch_pack_index(mask, B, L, cu_seqlens, token_rows, row_to_packed, max_seqlen,
+                                  stream);
+}
+
+static int gather_rows(const void* src, int64_t ld_src_bytes, int64_t n_src, const int32_t* index,
+                       int64_t n_rows, int64_t row_bytes, void* dst, int64_t ld_dst_bytes,
+                       bool zero_missing, hipStream_t stream) {
+  if (n_rows < 0 || n_src < 0 || row_bytes < 0) return DATTN_ERR_INVALID_ARGUMENT;
+  if (n_rows == 0 || row_bytes == 0) return DATTN_OK;
+  if (!src || !dst || !index) return DATTN_ERR_INVALID_ARGUMENT;
+  if (ld_src_bytes < row_bytes || ld_dst_bytes < row_bytes) return DATTN_ERR_INVALID_ARGUMENT;
+  if (row_bytes % 16 || ld_src_bytes % 16 || ld_dst_bytes % 16) return DATTN_ERR_UNSUPPORTED;
+  if (!aligned16(src) || !aligned16(dst)) return DATTN_ERR_UNSUPPORTED;
+  if (row_bytes / 16 > INT32_MAX) return DATTN_ERR_UNSUPPORTED;
+  return dattn::launch_gather_rows(src, ld_src_bytes, n_src, index, n_rows, row_bytes, dst,
+                                   ld_dst_bytes, zero_missing, stream);
+}
+
+int dattn_pack_rows(const void* src, int64_t ld_src_bytes, int64_t n_src,
+                    const int32_t* token_rows, int64_t n_rows, int64_t row_bytes, void* dst,
+                    int64_t ld_dst_bytes, hipStream_t stream) {
+  return gather_rows(src, ld_src_bytes, n_src, token_rows, n_rows, row_bytes, dst, ld_dst_bytes,
+                     false, stream);
+}
+
+int dattn_unpack_rows(const void* src, int64_t ld_src_bytes, int64_t n_src,
+                      const int32_t* row_to_packed, int64_t n_rows, int64_t row_bytes, void* dst,
+                      int64_t ld_dst_bytes, hipStream_t stream) {
+  return gather_rows(src, ld_src_bytes, n_src, row_to_packed, n_rows, row_bytes, dst,
+                     ld_dst_bytes, true, stream);
+}
+
 const char* dattn_strerror(int status) {
   switch (status) {
     case DATTN_OK: return "ok";

@@ -41,6 +41,18 @@ int launch_rel_bucket(int32_t* rel_idx, int32_t max_len, int32_t position_bucket
 // varlen = false: padded layout; true: packed layout.
 int launch_fwd(FwdParams& p, int dtype, int d, bool varlen, hipStream_t stream);
 
+// packing metadata of a [B, L] mask (null = all valid); max_len may be null
+int launch_pack_index(const uint8_t* mask, int32_t B, int32_t L, int32_t* cu,
+                      int32_t* token_rows, int32_t* row_to_packed, int32_t* max_len,
+                      hipStream_t stream);
+
+// dst row r <- src row idx[r] for r < n_rows; strides and row_bytes in
+// bytes (multiples of 16). Indices outside [0, n_src) skip the row, or zero
+// it when zero_missing.
+int launch_gather_rows(const void* src, int64_t ld_src, int64_t n_src, const int32_t* idx,
+                       int64_t n_rows, int64_t row_bytes, void* dst, int64_t ld_dst,
+                       bool zero_missing, hipStream_t stream);
+
 }  // namespace dattn
 
 #endif  // DATTN_INTERNAL_H

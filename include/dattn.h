@@ -149,6 +149,67 @@ int dattn_fwd_varlen(const void* q, const void* k, const void* v,
                      int32_t H, int32_t d, int32_t dtype,
                      uint32_t flags, float scale, hipStream_t stream);
 
+/*
+ * Packing a padded batch for dattn_fwd_varlen and back (DisentangledFlash
+ * README, "Packed unpadded inference": right-padded hidden states and their
+ * attention mask become FlashAttention-style [total_tokens, width] rows with
+ * int32 cu_seqlens; the metadata is reused by every encoder layer, and the
+ * packed outputs are returned to the padded layout). The README's benchmark
+ * notes that packing has a fixed cost, so it pays once padding is heavy.
+ *
+ * dattn_pack_index - build the packing metadata of a [B, L] mask.
+ *
+ * mask          : [B, L] bytes, nonzero = valid token, or NULL (all valid).
+ *                 Any pattern is accepted; valid tokens keep their order.
+ * cu_seqlens    : device int32[B + 1], written: cu[0] = 0 and cu[b+1] - cu[b]
+ *                 = valid tokens of row b. For a right-padded mask this is
+ *                 exactly the cu_seqlens dattn_fwd_varlen takes.
+ * token_rows    : device int32[B * L], written: entry r < cu[B] is the padded
+ *                 row b*L + l of the r-th valid token (row-major order);
+ *                 entries from cu[B] on are -1.
+ * row_to_packed : device int32[B * L], written: the packed index of padded
+ *                 row i, or -1 where the mask is zero.
+ * max_seqlen    : device int32[1] written with the longest row, or NULL.
+ * Work is three launches on `stream`; nothing is read back to the host, so
+ * a caller that needs cu[B] (to size the packed buffers) or max_seqlen on
+ * the host copies them itself. L is always a valid max_seqlen bound.
+ *
+ * Errors: INVALID_ARGUMENT (B < 0, L < 0, cu_seqlens NULL, or token_rows /
+ * row_to_packed NULL with B*L > 0); UNSUPPORTED (B*L > 2^31 - 1 or
+ * B = 2^31 - 1); HIP_ERROR. B == 0 writes cu[0] = 0 only.
+ */
+int dattn_pack_index(const uint8_t* mask, int32_t B, int32_t L, int32_t* cu_seqlens,
+                     int32_t* token_rows, int32_t* row_to_packed, int32_t* max_seqlen,
+                     hipStream_t stream);
+
+/*
+ * dattn_pack_rows - dst[r] = src[token_rows[r]] for r < n_rows.
+ *
+ * Rows are opaque bytes (any element type; a fused QKV row packs in one
+ * call). src has n_src rows of row_bytes bytes at stride ld_src_bytes; dst
+ * rows are at stride ld_dst_bytes. An index outside [0, n_src) (the -1
+ * tail of token_rows) leaves dst row r untouched, so with n_rows = B*L only
+ * the first cu[B] rows of dst are written and dst needs only that many.
+ *
+ * dattn_unpack_rows - dst[i] = src[row_to_packed[i]], or a zero row where
+ * the index is outside [0, n_src), for i < n_rows: every row of dst is
+ * written, padding rows with zeros.
+ *
+ * Both: pointers 16-byte aligned; row_bytes and both strides multiples of
+ * 16 bytes, strides >= row_bytes; src and dst must not overlap. Errors:
+ * INVALID_ARGUMENT (negative size or count, NULL pointer with n_rows > 0
+ * and row_bytes > 0, stride < row_bytes); UNSUPPORTED (alignment, a size
+ * not a multiple of 16 bytes); HIP_ERROR. n_rows == 0 or row_bytes == 0 is
+ * a no-op.
+ */
+int dattn_pack_rows(const void* src, int64_t ld_src_bytes, int64_t n_src,
+                    const int32_t* token_rows, int64_t n_rows, int64_t row_bytes, void* dst,
+                    int64_t ld_dst_bytes, hipStream_t stream);
+
+int dattn_unpack_rows(const void* src, int64_t ld_src_bytes, int64_t n_src,
+                      const int32_t* row_to_packed, int64_t n_rows, int64_t row_bytes, void* dst,
+                      int64_t ld_dst_bytes, hipStream_t stream);
+
 /* Static, human-readable text for a status code. */
 const char* dattn_strerror(int status);
 

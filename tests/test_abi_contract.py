@@ -120,3 +120,43 @@ def test_varlen_empty_is_noop(kw):
 ])
 def test_rel_bucket_rejections(args, status):
     assert dd.lib().rel_bucket(*args, None) == status
+
+
+def pack_index(**kw):
+    a = dict(mask=A, B=4, L=512, cu=A, token_rows=A, row_to_packed=A, max_seqlen=None,
+             stream=None)
+    a.update(kw)
+    return dd.lib().dattn_pack_index(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), INV), (dict(L=-1), INV), (dict(cu=None), INV), (dict(token_rows=None), INV),
+    (dict(row_to_packed=None), INV), (dict(B=1 << 16, L=1 << 16), UNS),
+])
+def test_pack_index_rejections(kw, status):
+    assert pack_index(**kw) == status
+
+
+def rows(fn, **kw):
+    a = dict(src=A, ld_src=3072, n_src=2048, index=A, n_rows=2048, row_bytes=3072, dst=A,
+             ld_dst=3072, stream=None)
+    a.update(kw)
+    return getattr(dd.lib(), fn)(*a.values())
+
+
+@pytest.mark.parametrize("fn", ["dattn_pack_rows", "dattn_unpack_rows"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(src=None), INV), (dict(dst=None), INV), (dict(index=None), INV),
+    (dict(n_rows=-1), INV), (dict(n_src=-1), INV), (dict(row_bytes=-16), INV),
+    (dict(ld_src=3056), INV), (dict(ld_dst=3056), INV),
+    (dict(row_bytes=3064, ld_src=3072, ld_dst=3072), UNS), (dict(ld_src=3080), UNS),
+    (dict(ld_dst=3080), UNS), (dict(src=MIS), UNS), (dict(dst=MIS), UNS),
+])
+def test_row_copy_rejections(fn, kw, status):
+    assert rows(fn, **kw) == status
+
+
+@pytest.mark.parametrize("fn", ["dattn_pack_rows", "dattn_unpack_rows"])
+@pytest.mark.parametrize("kw", [dict(n_rows=0), dict(row_bytes=0), dict(n_rows=0, src=None)])
+def test_row_copy_empty_is_noop(fn, kw):
+    assert rows(fn, **kw) == dd.DATTN_OK
