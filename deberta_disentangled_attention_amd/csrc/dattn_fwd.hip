@@ -182,8 +182,7 @@ struct Cfg {
   static constexpr int P1_BYTES = ES == 4 ? OFF_F + F_BYTES : 0;
   static constexpr int P_MAX = P1_BYTES > RING_BYTES ? P1_BYTES : RING_BYTES;
   static constexpr int OFF_C = P_MAX > G16_BYTES ? P_MAX : G16_BYTES;
-  static constexpr int OFF_CR = OFF_C + C_BYTES;     // c_j of three ring tiles
-  static constexpr int OFF_R = OFF_CR + 3 * C_BYTES;
+  static constexpr int OFF_R = OFF_C + C_BYTES;
   static constexpr int OFF_TW = OFF_R + R_BYTES;
   static constexpr int OFF_MISC = OFF_TW + TW_BYTES;
   static constexpr int LDS_BYTES = OFF_MISC + 64;
@@ -405,7 +404,6 @@ void dattn_fwd_kernel(FwdParams p) {
   float* Ew = reinterpret_cast<float*>(smem + C::OFF_E);
   float* Fw = reinterpret_cast<float*>(smem + C::OFF_F);
   float* cbuf = reinterpret_cast<float*>(smem + C::OFF_C);
-  float* cring = reinterpret_cast<float*>(smem + C::OFF_CR);
   unsigned char* Rrows = smem + C::OFF_R;   // qr_top, qr_bot, kr_top, kr_bot
   int* misc = reinterpret_cast<int*>(smem + C::OFF_MISC);
   uint32_t* Tw = reinterpret_cast<uint32_t*>(smem + C::OFF_TW);   // row offsets of a window of distances
@@ -1445,9 +1443,12 @@ void dattn_fwd_kernel(FwdParams p) {
 
     // ---- phase 2 (16-bit types): far tiles through the LDS ring -----------
     // Far tiles 0..FL-1 and FR..tm-1 are numbered n = 0, 1, ...; tile n lives
-    // in ring slot n % NSTAGE. Loads run three tiles ahead; c_j of tile n+1 is
-    // formed (by MFMA, 16 keys per wave) while tile n is computed; one barrier
-    // per tile publishes both.
+    // in ring slot n % NSTAGE. Loads run three tiles ahead and are waited for
+    // two steps after they are issued; one barrier per tile publishes them.
+    // On far tiles the P2C term is k_j . qr[row] with one saturated row per
+    // side, so it joins the Q.K product: the B operand is q_i + qr[row]
+    // (formed in fp32, rounded once to the element type), and one MFMA chain
+    // yields q_i.k_j + k_j.qr[row].
     const int nfar = FL + max(tm - FR, 0);
     if (nfar > 0) {
       auto far_tile = [&](int n) { return n < FL ? n : FR + (n - FL); };
@@ -1464,80 +1465,78 @@ void dattn_fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int x = 0; x < DPW; ++x) dma16(slot + C::KT_BYTES + 1024 * x, vt, vdo[x]);
       };
-      auto compute_c = [&](int n) {
-        c_group(kslot(n), wave, far_tile(n) < FL ? 1 : 0, cring + (n % 3) * BN);
+      // q_i + qr[row] (which: 0 top row, 1 bottom row) in this lane's layout
+      auto q_plus = [&](int which, uint4 (&dst)[NU]) {
+        uint4 rf[NU];
+        lds_half_row<NU>(rf, Rrows + which * D * ES + lh * C::HALF * ES);
+#pragma unroll
+        for (int x = 0; x < NU; ++x) {
+          const auto a = __builtin_bit_cast(typename Ty<T>::frag, qf[x]);
+          const auto b = __builtin_bit_cast(typename Ty<T>::frag, rf[x]);
+          f32x8_t sum;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sum[e] = (float)a[e] + (float)b[e];
+          dst[x] = __builtin_bit_cast(uint4, Ty<T>::cvt8(sum));
+        }
       };
 
-      // The loop is instantiated with and without the P2C term. It is
-      // software-pipelined: the scores of tile n+1 are produced by MFMAs
-      // issued in the same block as tile n's exponentials; c_j runs two
-      // tiles ahead so that those scores never wait for another wave.
-      auto ring_loop = [&](auto pc) {
-        constexpr bool PC = decltype(pc)::value;
-        auto scores = [&](int n, f32x16_t (&s)[C::NKB]) {
-          const unsigned char* ks = kslot(n);
-          const float* cb = cring + (n % 3) * BN;
+      // Software-pipelined: the scores of tile n+1 are produced by MFMAs
+      // issued in the same block as tile n's exponentials.
+      auto scores = [&](int n, const uint4 (&qop)[NU], f32x16_t (&s)[C::NKB]) {
+        const unsigned char* ks = kslot(n);
 #pragma unroll
-          for (int kb = 0; kb < C::NKB; ++kb) {
-            uint4 kf[NU];
-            k_operand(ks, kb, kf);
-            f32x16_t acc = f32x16_t{};
-            if constexpr (PC) acc = c_init(cb, kb);
-            s[kb] = mma_chain<T, NU, NC>(kf, qf, acc);
-          }
-        };
-        // tile n: scores in s_cur; produces the scores of tile n+1 in s_nxt
-        auto step = [&](int n, f32x16_t (&s_cur)[C::NKB], f32x16_t (&s_nxt)[C::NKB]) {
-          // c_j of tile n+1 (formed in the previous step) goes into s_nxt
-          // first, so its LDS reads have the exponentials to land
-          if constexpr (PC) {
-#pragma unroll
-            for (int kb = 0; kb < C::NKB; ++kb) s_nxt[kb] = c_init(cring + ((n + 1) % 3) * BN, kb);
-          }
-          if (n + C::NSTAGE - 1 < nfar) issue(n + C::NSTAGE - 1);   // into the slot of tile n-1
-          if (PC && n + 2 < nfar) compute_c(n + 2);
-          const float a_off = has_c2p ? (far_tile(n) < FL ? a_top : a_bot) : 0.f;
-          softmax_pv_mid(
-              s_cur, a_off, vop_slot(vslot(n)),
-              // unconditional, so the MFMAs share a block with the
-              // exponentials; after the last tile they read a stale slot
-              // and their result is not used
-              [&] {
-                const unsigned char* ks = kslot(n + 1);
-#pragma unroll
-                for (int kb = 0; kb < C::NKB; ++kb) {
-                  uint4 kf[NU];
-                  k_operand(ks, kb, kf);
-                  s_nxt[kb] = mma_chain<T, NU, NC>(kf, qf, PC ? s_nxt[kb] : f32x16_t{});
-                }
-              },
-              [&](f32x16_t (&sr)[C::NKB]) { scores(n, sr); });
-          // all of this wave's loads done: tile n+3 (and c_j of n+2) are
-          // visible after the barrier, and the slot of tile n is free
-          wait_vm<0>();
-          __syncthreads();
-        };
-
-        const int npre = min(nfar, C::NSTAGE - 1);
-        for (int n = 0; n < npre; ++n) issue(n);
-        wait_vm<0>();
-        __syncthreads();  // tiles 0 .. npre-1 in LDS
-        if constexpr (PC) {
-          compute_c(0);
-          if (nfar > 1) compute_c(1);
-          __syncthreads();  // c_j of tiles 0 and 1 visible
+        for (int kb = 0; kb < C::NKB; ++kb) {
+          uint4 kf[NU];
+          k_operand(ks, kb, kf);
+          s[kb] = mma_chain<T, NU, NC>(kf, qop, f32x16_t{});
         }
+      };
+      // tile n: scores in s_cur; produces the scores of tile n+1 in s_nxt
+      auto step = [&](int n, const uint4 (&qop)[NU], f32x16_t (&s_cur)[C::NKB],
+                      f32x16_t (&s_nxt)[C::NKB]) {
+        const bool more = n + C::NSTAGE - 1 < nfar;
+        if (more) issue(n + C::NSTAGE - 1);   // into the slot of tile n-1
+        const float a_off = has_c2p ? (far_tile(n) < FL ? a_top : a_bot) : 0.f;
+        softmax_pv_mid(
+            s_cur, a_off, vop_slot(vslot(n)),
+            // unconditional, so the MFMAs share a block with the exponentials;
+            // past the last tile of a run they read a slot whose result is
+            // not used
+            [&] { scores(n + 1, qop, s_nxt); },
+            [&](f32x16_t (&sr)[C::NKB]) { scores(n, qop, sr); });
+        // tile n+2, read from the next step on, has landed once at most the
+        // loads of tile n+3 are in flight; after the barrier it is visible
+        // and the slot of tile n is free
+        if (more) wait_vm<2 * DPW>();
+        else wait_vm<0>();
+        __syncthreads();
+      };
+      // tiles n0 .. n1-1 with B operand qop
+      auto run = [&](int n0, int n1, const uint4 (&qop)[NU]) {
+        if (n0 >= n1) return;
         f32x16_t sa[C::NKB], sb[C::NKB];
-        scores(0, sa);
-        int n = 0;
-        for (; n + 1 < nfar; n += 2) {
-          step(n, sa, sb);
-          step(n + 1, sb, sa);
+        scores(n0, qop, sa);
+        int n = n0;
+        for (; n + 1 < n1; n += 2) {
+          step(n, qop, sa, sb);
+          step(n + 1, qop, sb, sa);
         }
-        if (n < nfar) step(n, sa, sb);
+        if (n < n1) step(n, qop, sa, sb);
       };
-      if (has_p2c) ring_loop(std::true_type{});
-      else ring_loop(std::false_type{});
+
+      const int npre = min(nfar, C::NSTAGE - 1);
+      for (int n = 0; n < npre; ++n) issue(n);
+      wait_vm<0>();
+      __syncthreads();  // tiles 0 .. npre-1 in LDS
+      if (has_p2c) {
+        uint4 qop[NU];
+        q_plus(1, qop);   // keys left of the queries: bottom row
+        run(0, FL, qop);
+        q_plus(0, qop);   // keys right of the queries: top row
+        run(FL, nfar, qop);
+      } else {
+        run(0, nfar, qf);
+      }
     }
   }
 
