@@ -11,6 +11,7 @@ Modules:
   bucket    - relative-position bucket and row table, exact integers
   attention - scores, masked softmax and output per (sequence, head)
   pack      - padded <-> packed rows and their metadata
+  relproj   - the per-head projections qr, kr of the relative embeddings
 
 Pins (tests marked "not gpu") tie the modules to things other than
 themselves: exact integer identities and invariants of the bucket, a
@@ -21,7 +22,7 @@ under tests/golden/, mask / packing invariants, and packing examples
 worked by hand with a pure-Python brute force beside them.
 """
 
-from . import attention, bucket, pack  # noqa: F401
+from . import attention, bucket, pack, relproj  # noqa: F401
 from .attention import (C2P, P2C, dattn_padded, dattn_rows, dattn_varlen,  # noqa: F401
                         default_scale)
 from .bucket import log_bucket, rel_index_table, span  # noqa: F401
