@@ -3,6 +3,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4]
     python bench.py --pack [--workload c3]     # padded vs device-packed
+    python bench.py --relproj [--workload c2]  # qr/kr projection of that shape
 
 A step is one pass of the whole hot path over one batch of synthetic input:
 the relative-row table (rel_bucket) and the fused forward
@@ -291,6 +292,34 @@ def bench_pack(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_relproj(args):
+    """Time dattn_rel_proj on the workload's table shape: E [n_rel, H*d],
+    weights [H*d, H*d], both tables in one launch."""
+    import torch
+    import deberta_disentangled_attention_amd as dd
+    import workloads
+
+    w = build_workload(args.workload)
+    tdt = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+    hd = w.H * w.d
+    E, Wq, Wk, bq, bk = workloads.projection_inputs(0, w.n_rel, hd, hd, w.dtype)
+    dev = lambda x: torch.from_numpy(x).to(tdt).cuda()
+    E, Wq, Wk, bq, bk = dev(E), dev(Wq), dev(Wk), dev(bq), dev(bk)
+    qr = torch.empty((w.n_rel, hd), dtype=tdt, device="cuda")
+    kr = torch.empty_like(qr)
+    ms = _timed(lambda: dd.rel_proj(E, Wq, Wk, bq, bk, qr=qr, kr=kr), args.steps, args.warmup)
+    flop = 2 * 2.0 * w.n_rel * hd * hd
+    byts = (w.n_rel * hd + 2 * hd * hd + 2 * hd + 2 * w.n_rel * hd) * E.element_size()
+    peak = PEAK_TFLOPS[w.dtype]
+    print(json.dumps({
+        "metric": "relative-table projection (qr and kr, one launch)",
+        "workload": describe(w), "dtype": w.dtype, "n_rel": w.n_rel, "hidden": hd, "out": hd,
+        "steps": args.steps, "warmup": args.warmup, "ms": round(ms, 5),
+        "TFLOPs": round(flop / (ms * 1e-3) / 1e12, 2), "pct_mfma_peak": round(100 * flop / (ms * 1e-3) / 1e12 / peak, 2),
+        "GBps_min_bytes": round(byts / (ms * 1e-3) / 1e9, 1),
+    }), flush=True)
+
+
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--write-traffic":
         write_traffic(*sys.argv[2:6])
@@ -309,6 +338,8 @@ def main():
                     help="override the position terms (0 none, 1 C2P, 2 P2C, 3 both)")
     ap.add_argument("--pack", action="store_true",
                     help="padded forward vs the device-packed route on a padded workload")
+    ap.add_argument("--relproj", action="store_true",
+                    help="time the qr/kr projection of the workload's table shape")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -325,6 +356,11 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     dd.lib()
+    if args.relproj:
+        if args.workload == "c4":
+            args.workload = "c2"
+        bench_relproj(args)
+        return
     if args.pack:
         if args.workload == "c4":
             args.workload = "c3"

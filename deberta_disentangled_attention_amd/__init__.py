@@ -57,6 +57,9 @@ def lib() -> ctypes.CDLL:
         for fn in (h.dattn_pack_rows, h.dattn_unpack_rows):
             fn.argtypes = [vp, i64, i64, vp, i64, i64, vp, i64, vp]
             fn.restype = ctypes.c_int
+        h.dattn_rel_proj.argtypes = [vp, i64, vp, vp, i64, vp, vp, vp, vp, i64, i32, i32, i32, i32,
+                                     vp]
+        h.dattn_rel_proj.restype = ctypes.c_int
         h.dattn_strerror.argtypes = [ctypes.c_int]
         h.dattn_strerror.restype = ctypes.c_char_p
         _lib_handle = h
@@ -246,3 +249,34 @@ def unpack_rows(src, row_to_packed, B: int, L: int, *, out=None):
                                  _ptr(out), ld_dst, _stream(src))
     _check(st, "dattn_unpack_rows")
     return out
+
+
+def rel_proj(E, Wq, Wk, bq=None, bk=None, *, qr=None, kr=None):
+    """qr = E Wq^T + bq and kr = E Wk^T + bk in one launch. E is [n_rel,
+    hidden]; Wq, Wk are [H*d, hidden] (nn.Linear weights); biases [H*d] or
+    None. Returns (qr, kr), [n_rel, H*d] in E's dtype."""
+    import torch
+    n_rel, hidden = E.shape
+    HD = Wq.shape[0]
+    if Wk.shape != Wq.shape or Wq.shape[1] != hidden:
+        raise ValueError("Wq and Wk must be [H*d, hidden]")
+    if Wk.stride() != Wq.stride():
+        raise ValueError("Wq and Wk must have the same strides")
+    for name, t in (("E", E), ("Wq", Wq), ("Wk", Wk)):
+        if t.dtype != E.dtype:
+            raise ValueError(f"{name} must have E's dtype")
+    for name, t in (("bq", bq), ("bk", bk)):
+        if t is not None and (t.dtype != E.dtype or t.numel() != HD or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous [H*d] tensor of E's dtype")
+    if qr is None:
+        qr = torch.empty((n_rel, HD), dtype=E.dtype, device=E.device)
+    if kr is None:
+        kr = torch.empty((n_rel, HD), dtype=E.dtype, device=E.device)
+    if kr.stride() != qr.stride() or kr.shape != qr.shape:
+        raise ValueError("qr and kr must have the same shape and strides")
+    st = lib().dattn_rel_proj(_ptr(E), _row_stride(E, "E"), _ptr(Wq), _ptr(Wk),
+                              _row_stride(Wq, "Wq"), _ptr(bq), _ptr(bk), _ptr(qr), _ptr(kr),
+                              _row_stride(qr, "qr"), int(n_rel), int(hidden), int(HD),
+                              _dtype_code(E), _stream(E))
+    _check(st, "dattn_rel_proj")
+    return qr, kr

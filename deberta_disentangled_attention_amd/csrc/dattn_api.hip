@@ -150,6 +150,22 @@ int dattn_unpack_rows(const void* src, int64_t ld_src_bytes, int64_t n_src,
                      ld_dst_bytes, true, stream);
 }
 
+int dattn_rel_proj(const void* E, int64_t ld_e, const void* Wq, const void* Wk, int64_t ld_w,
+                   const void* bq, const void* bk, void* qr, void* kr, int64_t ld_out,
+                   int32_t n_rel, int32_t hidden, int32_t HD, int32_t dtype, hipStream_t stream) {
+  if (n_rel < 0 || hidden < 0 || HD < 0) return DATTN_ERR_INVALID_ARGUMENT;
+  if (dtype != DATTN_F32 && dtype != DATTN_F16 && dtype != DATTN_BF16) return DATTN_ERR_UNSUPPORTED;
+  if (n_rel == 0 || HD == 0) return DATTN_OK;
+  if (!E || !Wq || !Wk || !qr || !kr) return DATTN_ERR_INVALID_ARGUMENT;
+  if (ld_e < hidden || ld_w < hidden || ld_out < HD) return DATTN_ERR_INVALID_ARGUMENT;
+  if (hidden == 0 || hidden % 16) return DATTN_ERR_UNSUPPORTED;
+  const int es = esize_of(dtype);
+  if (!aligned16(E) || !aligned16(Wq) || !aligned16(Wk)) return DATTN_ERR_UNSUPPORTED;
+  if ((ld_e * es) % 16 || (ld_w * es) % 16) return DATTN_ERR_UNSUPPORTED;
+  return dattn::launch_rel_proj(E, ld_e, Wq, Wk, ld_w, bq, bk, qr, kr, ld_out, n_rel, hidden, HD,
+                                dtype, stream);
+}
+
 const char* dattn_strerror(int status) {
   switch (status) {
     case DATTN_OK: return "ok";

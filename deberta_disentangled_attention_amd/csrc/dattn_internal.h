@@ -53,6 +53,11 @@ int launch_gather_rows(const void* src, int64_t ld_src, int64_t n_src, const int
                        int64_t n_rows, int64_t row_bytes, void* dst, int64_t ld_dst,
                        bool zero_missing, hipStream_t stream);
 
+// qr = E Wq^T + bq, kr = E Wk^T + bk (biases may be null); strides in elements
+int launch_rel_proj(const void* E, int64_t ld_e, const void* Wq, const void* Wk, int64_t ld_w,
+                    const void* bq, const void* bk, void* qr, void* kr, int64_t ld_out,
+                    int32_t n_rel, int32_t hidden, int32_t HD, int dtype, hipStream_t stream);
+
 }  // namespace dattn
 
 #endif  // DATTN_INTERNAL_H

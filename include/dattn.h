@@ -150,6 +150,34 @@ int dattn_fwd_varlen(const void* q, const void* k, const void* v,
                      uint32_t flags, float scale, hipStream_t stream);
 
 /*
+ * dattn_rel_proj - the per-head relative tables from the relative embeddings:
+ *
+ *   qr = E Wq^T + bq,   kr = E Wk^T + bk
+ *
+ * In DeBERTa-v2/v3 (the models the DisentangledFlash README's "Attribution"
+ * section names) qr and kr are the attention layer's query and key linear
+ * maps applied to the relative-embedding table that the whole batch
+ * shares; the forward then reads their rows through rel_idx.
+ *
+ * E       : [n_rel, hidden] relative embeddings, row stride ld_e.
+ * Wq, Wk  : [HD, hidden] weights in nn.Linear layout (one output feature per
+ *           row), row stride ld_w; HD = H*d.
+ * bq, bk  : [HD] biases, or NULL (zero).
+ * qr, kr  : [n_rel, HD] outputs, row stride ld_out; exactly the arrays
+ *           dattn_fwd_padded / dattn_fwd_varlen take (n_rel rows).
+ * All arrays have element type dtype; products accumulate in fp32 and each
+ * output is rounded once. One launch on `stream` writes both tables.
+ *
+ * Errors: INVALID_ARGUMENT (negative size, NULL array when n_rel*HD > 0,
+ * ld_e or ld_w < hidden, ld_out < HD); UNSUPPORTED (dtype, hidden not a
+ * positive multiple of 16, E/Wq/Wk misaligned or strides not multiples of
+ * 16 bytes); HIP_ERROR. n_rel == 0 or HD == 0 is a no-op.
+ */
+int dattn_rel_proj(const void* E, int64_t ld_e, const void* Wq, const void* Wk, int64_t ld_w,
+                   const void* bq, const void* bk, void* qr, void* kr, int64_t ld_out,
+                   int32_t n_rel, int32_t hidden, int32_t HD, int32_t dtype, hipStream_t stream);
+
+/*
  * Packing a padded batch for dattn_fwd_varlen and back (DisentangledFlash
  * README, "Packed unpadded inference": right-padded hidden states and their
  * attention mask become FlashAttention-style [total_tokens, width] rows with

@@ -160,3 +160,26 @@ def test_row_copy_rejections(fn, kw, status):
 @pytest.mark.parametrize("kw", [dict(n_rows=0), dict(row_bytes=0), dict(n_rows=0, src=None)])
 def test_row_copy_empty_is_noop(fn, kw):
     assert rows(fn, **kw) == dd.DATTN_OK
+
+
+def rel_proj(**kw):
+    a = dict(E=A, ld_e=768, Wq=A, Wk=A, ld_w=768, bq=None, bk=None, qr=A, kr=A, ld_out=768,
+             n_rel=512, hidden=768, HD=768, dtype=2, stream=None)
+    a.update(kw)
+    return dd.lib().dattn_rel_proj(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_rel=-1), INV), (dict(hidden=-16), INV), (dict(HD=-1), INV), (dict(E=None), INV),
+    (dict(Wq=None), INV), (dict(Wk=None), INV), (dict(qr=None), INV), (dict(kr=None), INV),
+    (dict(ld_e=700), INV), (dict(ld_w=700), INV), (dict(ld_out=700), INV),
+    (dict(dtype=5), UNS), (dict(hidden=760, ld_e=768, ld_w=768), UNS), (dict(hidden=0), UNS),
+    (dict(E=MIS), UNS), (dict(Wk=MIS), UNS), (dict(ld_e=772), UNS), (dict(dtype=0, ld_w=770), UNS),
+])
+def test_rel_proj_rejections(kw, status):
+    assert rel_proj(**kw) == status
+
+
+@pytest.mark.parametrize("kw", [dict(n_rel=0), dict(HD=0), dict(n_rel=0, E=None)])
+def test_rel_proj_empty_is_noop(kw):
+    assert rel_proj(**kw) == dd.DATTN_OK

@@ -175,6 +175,23 @@ def relative_tables(rng: np.random.Generator, n_rel: int, H: int, d: int, dtype:
     return qr, kr
 
 
+def projection_inputs(seed: int, n_rel: int, hidden: int, HD: int, dtype: str,
+                      bias: bool = True):
+    """Relative embeddings and projection weights for the table projection:
+    E ~ N(0, 0.02^2) [n_rel, hidden]; Wq, Wk ~ N(0, s^2) [HD, hidden]
+    (nn.Linear layout) with s = 1/(0.02 sqrt(hidden)), so the projected
+    entries have unit variance; biases ~ N(0, 0.1^2) [HD] or None. All
+    rounded to dtype (float32 arrays holding exact values)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    E = round_to(_normals(rng, (n_rel, hidden), 0.02), dtype)
+    s = 1.0 / (0.02 * math.sqrt(hidden))
+    Wq = round_to(_normals(rng, (HD, hidden), s), dtype)
+    Wk = round_to(_normals(rng, (HD, hidden), s), dtype)
+    bq = round_to(_normals(rng, (HD,), 0.1), dtype) if bias else None
+    bk = round_to(_normals(rng, (HD,), 0.1), dtype) if bias else None
+    return E, Wq, Wk, bq, bk
+
+
 def make_workload(name: str, *, dtype: str, B: int, L: int, H: int, d: int,
                   position_buckets: int, max_relative_positions: int,
                   lens: Optional[np.ndarray] = None, seed: int = 0,
