@@ -6,19 +6,18 @@
 // attention layer's own query and key maps applied to the relative
 // embeddings.
 //
-// One launch forms both tables. A workgroup owns a 32 x 32 output block of
-// one table (blockIdx.z: 0 = qr, 1 = kr); its four waves split the hidden
-// dimension (wave w takes 16-element chunks w, w+4, ...), each accumulating
-// a 32x32 MFMA product in fp32, and the partial blocks are summed through
-// LDS. The problem is small (a v3-base table is 2 x 0.6 GFLOP), so the split
-// is what keeps enough loads in flight: each wave loads its next group of
-// chunks while it multiplies the current one. Both operands keep the
-// reduction dimension contiguous in memory, so every lane reads its operand
-// fragment straight from global memory as 16-byte units: within a chunk,
-// lane half h supplies elements 8h .. 8h+7 for both operands, which pairs A
-// and B elements of the same index. Rows and columns past the ends are read
-// clamped and not stored. The bias is added and the result rounded once to
-// the element type.
+// One launch forms both tables. A workgroup owns a 64 x 64 output tile of
+// one table (blockIdx.z: 0 = qr, 1 = kr) and each of its four waves a
+// 32 x 32 block, accumulated by 32x32 MFMAs in fp32. The reduction runs in
+// stages of 256 bytes of every row: the workgroup's 64 rows of E and of W
+// for a stage go to LDS (double-buffered; the next stage is loaded into
+// registers while the current one is multiplied), so each row is read from
+// L2 once per tile rather than once per wave. Both operands keep the
+// reduction dimension contiguous: within a 16-element chunk, lane half h
+// supplies elements 8h .. 8h+7 of both, which pairs A and B elements of the
+// same index. Rows and columns past the ends are read clamped and not
+// stored; a partly full last stage is zero-filled. The bias is added and
+// the result rounded once to the element type.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -33,13 +32,11 @@ typedef __bf16 rp_bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 rp_f16x8 __attribute__((ext_vector_type(8)));
 typedef float rp_f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int RP_TILE = 32;
-constexpr int RP_CHUNK = 16;   // reduction elements per step
-#ifndef RP_UNROLL_STEPS
-#define RP_UNROLL_STEPS 4
+constexpr int RP_TILE = 64;    // output rows and columns of a workgroup
+constexpr int RP_CHUNK = 16;   // reduction elements per MFMA step group
+#ifndef RP_STAGE_BYTES
+#define RP_STAGE_BYTES 256     // bytes of every row staged in LDS per step
 #endif
-constexpr int RP_UNROLL = RP_UNROLL_STEPS;   // steps whose loads are issued together
-constexpr int RP_WAVES = 4;    // waves splitting the reduction
 
 struct RelProjParams {
   const unsigned char* E;
@@ -102,72 +99,83 @@ template <> struct RP<2> {     // bf16: one 32x32x16 step per chunk
 };
 
 template <int DT>
-__global__ __launch_bounds__(64 * RP_WAVES) void rel_proj_kernel(const RelProjParams p) {
+__global__ __launch_bounds__(256) void rel_proj_kernel(const RelProjParams p) {
   typedef RP<DT> R;
   constexpr int ES = R::ES, U = R::U;
-  __shared__ float part[RP_WAVES - 1][16][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int SB = RP_STAGE_BYTES;      // bytes of a row per stage
+  constexpr int UPR = SB / 16;            // 16-byte units of a row per stage
+  constexpr int UPT = SB / 64;            // units per thread per tile and stage
+  constexpr int CB = RP_CHUNK * ES;       // bytes of a 16-element chunk
+  constexpr int PITCH = SB + 16;          // LDS row pitch (bytes)
+  static_assert(SB % CB == 0 && UPT >= 1, "stage size");
+  __shared__ __align__(16) unsigned char lds[2][2][RP_TILE * PITCH];   // [buffer][E, W][row]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 31, lh = lane >> 5;
+  const int wr = wave >> 1, wc = wave & 1;   // this wave's 32 x 32 block of the tile
   const int z = blockIdx.z;
   const int r0 = blockIdx.y * RP_TILE, o0 = blockIdx.x * RP_TILE;
-  // this lane's operand rows, clamped into the arrays
-  const int ra = min(r0 + li, p.n_rel - 1), oa = min(o0 + li, p.HD - 1);
-  const unsigned char* ea = p.E + (int64_t)ra * p.ld_e * ES + 8 * lh * ES;
-  const unsigned char* wa = p.W[z] + (int64_t)oa * p.ld_w * ES + 8 * lh * ES;
-
-  const int nchunk = p.hidden / RP_CHUNK;
-  // group g of this wave: chunks (g * RP_UNROLL + s) * RP_WAVES + wave
-  const int per_group = RP_UNROLL * RP_WAVES;
-  const int ngroups = (nchunk + per_group - 1) / per_group;
-  typedef uint4 Ops[RP_UNROLL][U];
-  auto load_group = [&](int g, Ops& a, Ops& b) {
+  // loader: unit x = t + 256 j (j < UPT) of a tile is 16-byte unit x % UPR of
+  // row x / UPR; both tiles, rows read clamped into the arrays
+  const unsigned char* ga[UPT];
+  const unsigned char* gb[UPT];
+  int lrow[UPT], lu[UPT];
 #pragma unroll
-    for (int s = 0; s < RP_UNROLL; ++s) {
-      const int c = (g * RP_UNROLL + s) * RP_WAVES + wave;
+  for (int j = 0; j < UPT; ++j) {
+    const int x = tid + 256 * j;
+    lrow[j] = x / UPR;
+    lu[j] = x % UPR;
+    ga[j] = p.E + (int64_t)min(r0 + lrow[j], p.n_rel - 1) * p.ld_e * ES;
+    gb[j] = p.W[z] + (int64_t)min(o0 + lrow[j], p.HD - 1) * p.ld_w * ES;
+  }
+  const int64_t row_bytes = (int64_t)p.hidden * ES;
+  const int nst = (int)((row_bytes + SB - 1) / SB);
+  uint4 va[UPT], vb[UPT];
+  auto fetch = [&](int st) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (c < nchunk) {
-          a[s][u] = ldg16(ea + ((int64_t)c * RP_CHUNK) * ES + 16 * u);
-          b[s][u] = ldg16(wa + ((int64_t)c * RP_CHUNK) * ES + 16 * u);
-        } else {
-          a[s][u] = make_uint4(0, 0, 0, 0);
-          b[s][u] = make_uint4(0, 0, 0, 0);
-        }
-      }
+    for (int j = 0; j < UPT; ++j) {
+      const int64_t off = (int64_t)st * SB + 16 * lu[j];
+      const bool in = off < row_bytes;   // the last stage may be partly full
+      va[j] = in ? ldg16(ga[j] + off) : make_uint4(0, 0, 0, 0);
+      vb[j] = in ? ldg16(gb[j] + off) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto put = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < UPT; ++j) {
+      *reinterpret_cast<uint4*>(&lds[buf][0][lrow[j] * PITCH + 16 * lu[j]]) = va[j];
+      *reinterpret_cast<uint4*>(&lds[buf][1][lrow[j] * PITCH + 16 * lu[j]]) = vb[j];
     }
   };
   rp_f32x16 acc = {};
-  auto mult = [&](const Ops& a, const Ops& b) {
+  fetch(0);
+  put(0);
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < nst) fetch(st + 1);
+    const unsigned char* la = &lds[buf][0][(32 * wr + li) * PITCH + 8 * lh * ES];
+    const unsigned char* lb = &lds[buf][1][(32 * wc + li) * PITCH + 8 * lh * ES];
 #pragma unroll
-    for (int s = 0; s < RP_UNROLL; ++s) acc = R::step(a[s], b[s], acc);
-  };
-  Ops a0, b0, a1, b1;
-  if (ngroups > 0) load_group(0, a0, b0);
-  for (int g = 0; g < ngroups; g += 2) {
-    if (g + 1 < ngroups) load_group(g + 1, a1, b1);
-    mult(a0, b0);
-    if (g + 2 < ngroups) load_group(g + 2, a0, b0);
-    if (g + 1 < ngroups) mult(a1, b1);
+    for (int c = 0; c < SB / CB; ++c) {
+      uint4 a[U], b[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        a[u] = *reinterpret_cast<const uint4*>(la + c * CB + 16 * u);
+        b[u] = *reinterpret_cast<const uint4*>(lb + c * CB + 16 * u);
+      }
+      acc = R::step(a, b, acc);
+    }
+    if (st + 1 < nst) put(buf ^ 1);
+    __syncthreads();   // the next stage is in; this one may be overwritten
   }
 
-  // partial blocks of waves 1.. through LDS; wave 0 sums and stores
-  if (wave > 0) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) part[wave - 1][r][lane] = acc[r];
-  }
-  __syncthreads();
-  if (wave > 0) return;
-#pragma unroll
-  for (int w = 0; w < RP_WAVES - 1; ++w)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] += part[w][r][lane];
-  // lane: output column o0 + li; register r: row r0 + 8 (r / 4) + 4 lh + r % 4
-  const int o = o0 + li;
+  // lane: output column; register r: row 8 (r / 4) + 4 lh + r % 4 of the block
+  const int o = o0 + 32 * wc + li;
   if (o >= p.HD) return;
   const float bias = p.bias[z] ? R::load(p.bias[z] + (int64_t)o * ES) : 0.f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const int row = r0 + 8 * (r >> 2) + 4 * lh + (r & 3);
+    const int row = r0 + 32 * wr + 8 * (r >> 2) + 4 * lh + (r & 3);
     if (row < p.n_rel) R::store(p.out[z] + ((int64_t)row * p.ld_out + o) * ES, acc[r] + bias);
   }
 }
@@ -192,7 +200,7 @@ int launch_rel_proj(const void* E, int64_t ld_e, const void* Wq, const void* Wk,
   p.hidden = hidden;
   p.HD = HD;
   const dim3 grid((HD + RP_TILE - 1) / RP_TILE, (n_rel + RP_TILE - 1) / RP_TILE, 2);
-  const dim3 block(64 * RP_WAVES);
+  const dim3 block(256);
   if (dtype == 0) hipLaunchKernelGGL(rel_proj_kernel<0>, grid, block, 0, stream, p);
   else if (dtype == 1) hipLaunchKernelGGL(rel_proj_kernel<1>, grid, block, 0, stream, p);
   else hipLaunchKernelGGL(rel_proj_kernel<2>, grid, block, 0, stream, p);
