@@ -12,6 +12,7 @@ Modules:
   attention - scores, masked softmax and output per (sequence, head)
   pack      - padded <-> packed rows and their metadata
   relproj   - the per-head projections qr, kr of the relative embeddings
+  backward  - gradients of the forward (and the row log-sum-exp)
 
 Pins (tests marked "not gpu") tie the modules to things other than
 themselves: exact integer identities and invariants of the bucket, a
@@ -22,7 +23,7 @@ under tests/golden/, mask / packing invariants, and packing examples
 worked by hand with a pure-Python brute force beside them.
 """
 
-from . import attention, bucket, pack, relproj  # noqa: F401
+from . import attention, backward, bucket, pack, relproj  # noqa: F401
 from .attention import (C2P, P2C, dattn_padded, dattn_rows, dattn_varlen,  # noqa: F401
                         default_scale)
 from .bucket import log_bucket, rel_index_table, span  # noqa: F401
