@@ -12,7 +12,8 @@
 //   token_rows[r]     = padded row b*L + l of the r-th valid token in
 //                       row-major order, -1 for r >= cu[B]
 //   row_to_packed[i]  = r with token_rows[r] = i, or -1
-// built by three small launches:
+// built in one workgroup for batches up to 4096 rows and 2^18 tokens
+// (pack_index_small_kernel), otherwise by three launches:
 //   pack_rank_kernel  one workgroup per row: each valid token's rank among
 //                     the row's valid tokens (a prefix count of the mask by
 //                     wave ballots), and the row's count
@@ -118,6 +119,84 @@ __global__ void pack_place_kernel(int32_t B, int32_t L, int64_t n, const int32_t
   if (i >= cu[B]) token_rows[i] = -1;
 }
 
+// The whole index in one workgroup, for small batches (one launch instead of
+// three): wave w counts rows w, w + 16, ...; the counts are scanned in LDS;
+// the waves then revisit their rows to place every token.
+constexpr int SMALL_THREADS = 1024;
+constexpr int SMALL_MAX_ROWS = 4096;
+constexpr int64_t SMALL_MAX_TOKENS = 1 << 18;
+
+__global__ __launch_bounds__(SMALL_THREADS) void pack_index_small_kernel(
+    const uint8_t* __restrict__ mask, int32_t B, int32_t L, int32_t* __restrict__ cu,
+    int32_t* __restrict__ token_rows, int32_t* __restrict__ row_to_packed,
+    int32_t* __restrict__ max_len) {
+  __shared__ int start[SMALL_MAX_ROWS + 1];
+  __shared__ int wave_sum[SMALL_THREADS / 64];
+  __shared__ int wave_max[SMALL_THREADS / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int NWAVE = SMALL_THREADS / 64;
+  const uint64_t below_me = (1ull << lane) - 1ull;
+  auto valid_at = [&](int64_t row0, int l) {
+    return l < L && (mask == nullptr || mask[row0 + l] != 0);
+  };
+  // counts of the rows
+  for (int b = wave; b < B; b += NWAVE) {
+    const int64_t row0 = (int64_t)b * L;
+    int n = 0;
+    for (int l0 = 0; l0 < L; l0 += 64) n += __popcll(__ballot(valid_at(row0, l0 + lane)));
+    if (lane == 0) start[b + 1] = n;
+  }
+  __syncthreads();
+  // running sums (one chunk of SMALL_THREADS rows at a time) and the maximum
+  int carry = 0, longest = 0;
+  for (int b0 = 0; b0 < B; b0 += SMALL_THREADS) {
+    const int b = b0 + tid;
+    const int c = b < B ? start[b + 1] : 0;
+    int x = c, m = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o);
+      x += lane >= o ? y : 0;
+      m = max(m, __shfl_xor(m, o));
+    }
+    if (lane == 63) wave_sum[wave] = x;
+    if (lane == 0) wave_max[wave] = m;
+    __syncthreads();
+    int before = carry, chunk = 0, cm = 0;
+#pragma unroll
+    for (int w = 0; w < NWAVE; ++w) {
+      before += w < wave ? wave_sum[w] : 0;
+      chunk += wave_sum[w];
+      cm = max(cm, wave_max[w]);
+    }
+    __syncthreads();   // every count of this chunk is read before it is overwritten
+    if (b < B) start[b + 1] = before + x;
+    carry += chunk;
+    longest = max(longest, cm);
+  }
+  if (tid == 0) start[0] = 0;
+  __syncthreads();
+  for (int b = tid; b <= B; b += SMALL_THREADS) cu[b] = start[b];
+  if (tid == 0 && max_len) *max_len = longest;
+  // place the tokens
+  for (int b = wave; b < B; b += NWAVE) {
+    const int64_t row0 = (int64_t)b * L;
+    int r = start[b];
+    for (int l0 = 0; l0 < L; l0 += 64) {
+      const int l = l0 + lane;
+      const bool valid = valid_at(row0, l);
+      const uint64_t bal = __ballot(valid);
+      const int p = r + __popcll(bal & below_me);
+      if (l < L) row_to_packed[row0 + l] = valid ? p : -1;
+      if (valid) token_rows[p] = (int32_t)(row0 + l);
+      r += __popcll(bal);
+    }
+  }
+  // entries at or beyond the packed total
+  const int64_t n = (int64_t)B * L;
+  for (int64_t i = start[B] + tid; i < n; i += SMALL_THREADS) token_rows[i] = -1;
+}
+
 // dst row r <- src row idx[r]; an index outside [0, n_src) leaves the row
 // untouched (ZERO = false) or writes zeros (ZERO = true).
 template <bool ZERO>
@@ -155,6 +234,11 @@ __global__ __launch_bounds__(GATHER_THREADS) void gather_rows_kernel(
 int launch_pack_index(const uint8_t* mask, int32_t B, int32_t L, int32_t* cu,
                       int32_t* token_rows, int32_t* row_to_packed, int32_t* max_len,
                       hipStream_t stream) {
+  if (B <= SMALL_MAX_ROWS && (int64_t)B * L <= SMALL_MAX_TOKENS) {
+    hipLaunchKernelGGL(pack_index_small_kernel, dim3(1), dim3(SMALL_THREADS), 0, stream, mask, B,
+                       L, cu, token_rows, row_to_packed, max_len);
+    return hipGetLastError() == hipSuccess ? 0 : 3;
+  }
   if (B > 0)
     hipLaunchKernelGGL(pack_rank_kernel, dim3(B), dim3(RANK_THREADS), 0, stream, mask, L, cu,
                        row_to_packed);

@@ -3,8 +3,9 @@
 Index arrays (cu_seqlens, token_rows, row_to_packed, max_seqlen) and the
 copied rows must equal oracle/pack.py exactly. Masks cover right padding,
 holes, empty rows, all-valid and NULL, lengths that are not multiples of
-the 256-token chunk, more rows than the scan's 1024-entry chunk, and the
-longest supported sequence. Row widths cover 16 bytes, widths below one
+the 64- and 256-token chunks, more rows than the scans' 1024-entry chunk,
+the longest supported sequence, and batches on both sides of the
+one-workgroup path's limits. Row widths cover 16 bytes, widths below one
 wave's 1024 bytes, exact multiples, and fused-QKV rows that take the
 four-deep copy loop plus a tail. The end-to-end case packs the c3 batch
 (deberta-v2-xlarge shape, 92.6% padding) on the device, runs the packed
@@ -57,7 +58,9 @@ def _gpu_index(mask, B, L):
 
 @pytest.mark.parametrize("kind", ["right", "holes", "empty_rows", "zeros", "ones", "null"])
 @pytest.mark.parametrize("B,L", [(1, 1), (3, 37), (16, 512), (5, 300), (1500, 3), (2, 8192),
-                                 (7, 257), (1, 0), (0, 5)])
+                                 (7, 257), (1, 0), (0, 5),
+                                 # past the one-workgroup limits (4096 rows, 2^18 tokens)
+                                 (5000, 3), (64, 8192), (4096, 64), (4097, 1)])
 def test_pack_index_bit_exact(kind, B, L):
     _say(f"pack_index {kind} B={B} L={L}")
     mask = _mask(kind, B, L, seed=B * 131 + L)
