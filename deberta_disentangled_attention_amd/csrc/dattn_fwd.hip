@@ -274,7 +274,12 @@ __device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32);
 
 // Direct-to-LDS load (global_load_lds_dwordx4): lane i's 16 bytes at
 // gbase + voff are written to LDS byte address lds + 16 i. The data bypasses
-// the registers; completion is tracked by this wave's vmcnt.
+// the registers; completion is tracked by this wave's vmcnt. Inline assembly
+// rather than the compiler's builtin for this load: with the builtin, the
+// compiler waits for every outstanding direct load (vmcnt(0)) before any LDS
+// read it cannot prove disjoint, which would serialise the ring below; the
+// explicit waits (wait_vm) keep the newest loads in flight instead. m0 is
+// set here and declared clobbered; nothing else in these kernels uses it.
 __device__ __forceinline__ void dma16(uint32_t lds, const void* gbase, uint32_t voff) {
   const uint64_t g = (uint64_t)(size_t)gbase;
   const uint64_t gu = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(g >> 32)) << 32) |
