@@ -162,6 +162,11 @@ int dattn_rel_proj(const void* E, int64_t ld_e, const void* Wq, const void* Wk, 
   const int es = esize_of(dtype);
   if (!aligned16(E) || !aligned16(Wq) || !aligned16(Wk)) return DATTN_ERR_UNSUPPORTED;
   if ((ld_e * es) % 16 || (ld_w * es) % 16) return DATTN_ERR_UNSUPPORTED;
+  // outputs and biases are accessed one element at a time
+  const auto elem_ok = [es](const void* ptr) {
+    return ptr == nullptr || (reinterpret_cast<uintptr_t>(ptr) % (uintptr_t)es) == 0;
+  };
+  if (!elem_ok(qr) || !elem_ok(kr) || !elem_ok(bq) || !elem_ok(bk)) return DATTN_ERR_UNSUPPORTED;
   return dattn::launch_rel_proj(E, ld_e, Wq, Wk, ld_w, bq, bk, qr, kr, ld_out, n_rel, hidden, HD,
                                 dtype, stream);
 }

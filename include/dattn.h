@@ -170,8 +170,9 @@ int dattn_fwd_varlen(const void* q, const void* k, const void* v,
  *
  * Errors: INVALID_ARGUMENT (negative size, NULL array when n_rel*HD > 0,
  * ld_e or ld_w < hidden, ld_out < HD); UNSUPPORTED (dtype, hidden not a
- * positive multiple of 16, E/Wq/Wk misaligned or strides not multiples of
- * 16 bytes); HIP_ERROR. n_rel == 0 or HD == 0 is a no-op.
+ * positive multiple of 16, E/Wq/Wk not 16-byte aligned or their strides not
+ * multiples of 16 bytes, qr/kr/bq/bk not aligned to the element size);
+ * HIP_ERROR. n_rel == 0 or HD == 0 is a no-op.
  */
 int dattn_rel_proj(const void* E, int64_t ld_e, const void* Wq, const void* Wk, int64_t ld_w,
                    const void* bq, const void* bk, void* qr, void* kr, int64_t ld_out,

@@ -175,6 +175,8 @@ def rel_proj(**kw):
     (dict(ld_e=700), INV), (dict(ld_w=700), INV), (dict(ld_out=700), INV),
     (dict(dtype=5), UNS), (dict(hidden=760, ld_e=768, ld_w=768), UNS), (dict(hidden=0), UNS),
     (dict(E=MIS), UNS), (dict(Wk=MIS), UNS), (dict(ld_e=772), UNS), (dict(dtype=0, ld_w=770), UNS),
+    (dict(qr=A + 1), UNS), (dict(kr=A + 1), UNS), (dict(bq=A + 1), UNS),
+    (dict(dtype=0, kr=A + 2), UNS), (dict(dtype=0, bk=A + 2), UNS),
 ])
 def test_rel_proj_rejections(kw, status):
     assert rel_proj(**kw) == status
