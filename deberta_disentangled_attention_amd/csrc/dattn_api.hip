@@ -12,6 +12,8 @@
 namespace {
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+// int32 arrays are read and written as whole words
+bool aligned4(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 3u) == 0; }
 
 int esize_of(int32_t dtype) { return dtype == DATTN_F32 ? 4 : 2; }
 
@@ -34,6 +36,7 @@ int check_common(const void* q, const void* k, const void* v, int64_t ld_q, int6
   if ((ld_q * es) % 16 || (ld_k * es) % 16 || (ld_v * es) % 16) return DATTN_ERR_UNSUPPORTED;
   if (flags) {
     if (!qr || !kr || !rel_idx) return DATTN_ERR_INVALID_ARGUMENT;
+    if (!aligned4(rel_idx)) return DATTN_ERR_UNSUPPORTED;
     if (n_rel < 1 || ld_rel < hd) return DATTN_ERR_INVALID_ARGUMENT;
     if (rel_max_len < seq_bound || rel_max_len < 1) return DATTN_ERR_INVALID_ARGUMENT;
     if (!aligned16(qr) || !aligned16(kr) || (ld_rel * es) % 16) return DATTN_ERR_UNSUPPORTED;
@@ -55,6 +58,7 @@ extern "C" {
 int rel_bucket(int32_t* rel_idx, int32_t max_len, int32_t position_buckets,
                int32_t max_relative_positions, hipStream_t stream) {
   if (!rel_idx || max_len < 1) return DATTN_ERR_INVALID_ARGUMENT;
+  if (!aligned4(rel_idx)) return DATTN_ERR_UNSUPPORTED;
   if (max_len > 65536) return DATTN_ERR_UNSUPPORTED;
   if (position_buckets > 0) {
     const int mid = position_buckets / 2;
@@ -95,6 +99,7 @@ int dattn_fwd_varlen(const void* q, const void* k, const void* v, int64_t ld_q, 
                      int32_t d, int32_t dtype, uint32_t flags, float scale, hipStream_t stream) {
   if (nseq < 0 || total_tokens < 0 || max_seqlen < 0) return DATTN_ERR_INVALID_ARGUMENT;
   if (!cu_seqlens) return DATTN_ERR_INVALID_ARGUMENT;
+  if (!aligned4(cu_seqlens)) return DATTN_ERR_UNSUPPORTED;
   int st = check_common(q, k, v, ld_q, ld_k, ld_v, qr, kr, ld_rel, n_rel, rel_idx, rel_max_len,
                         out, H, d, dtype, flags, scale, max_seqlen);
   if (st != DATTN_OK) return st;
@@ -118,6 +123,9 @@ int dattn_pack_index(const uint8_t* mask, int32_t B, int32_t L, int32_t* cu_seql
   const int64_t n = (int64_t)B * L;
   if (n > INT32_MAX || B == INT32_MAX) return DATTN_ERR_UNSUPPORTED;  // int32 indices
   if (n > 0 && (!token_rows || !row_to_packed)) return DATTN_ERR_INVALID_ARGUMENT;
+  if (!aligned4(cu_seqlens) || !aligned4(token_rows) || !aligned4(row_to_packed) ||
+      !aligned4(max_seqlen))
+    return DATTN_ERR_UNSUPPORTED;
   return dattn::launch_pack_index(mask, B, L, cu_seqlens, token_rows, row_to_packed, max_seqlen,
                                   stream);
 }
@@ -128,6 +136,7 @@ static int gather_rows(const void* src, int64_t ld_src_bytes, int64_t n_src, con
   if (n_rows < 0 || n_src < 0 || row_bytes < 0) return DATTN_ERR_INVALID_ARGUMENT;
   if (n_rows == 0 || row_bytes == 0) return DATTN_OK;
   if (!src || !dst || !index) return DATTN_ERR_INVALID_ARGUMENT;
+  if (!aligned4(index)) return DATTN_ERR_UNSUPPORTED;
   if (ld_src_bytes < row_bytes || ld_dst_bytes < row_bytes) return DATTN_ERR_INVALID_ARGUMENT;
   if (row_bytes % 16 || ld_src_bytes % 16 || ld_dst_bytes % 16) return DATTN_ERR_UNSUPPORTED;
   if (!aligned16(src) || !aligned16(dst)) return DATTN_ERR_UNSUPPORTED;

@@ -32,6 +32,8 @@
  *   - Row strides (ld_*) are in elements, must be >= H*d and a multiple of
  *     16 bytes; every array pointer must be 16-byte aligned. A fused QKV
  *     buffer [tokens, 3*H*d] is passed as three pointers with ld = 3*H*d.
+ *   - int32 arrays (tables, cu_seqlens, packing metadata) must be 4-byte
+ *     aligned (UNSUPPORTED otherwise).
  *   - No hidden fallback: an unsupported case returns DATTN_ERR_UNSUPPORTED
  *     and the caller decides what to do.
  */

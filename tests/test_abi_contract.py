@@ -83,6 +83,7 @@ def varlen(**kw):
     (dict(dtype=0, ld_q=770), UNS),
     # relative tables whose row offsets would not fit in 31 bits
     (dict(n_rel=1 << 20, ld_rel=1 << 10), UNS), (dict(n_rel=1 << 20, ld_rel=1 << 10, flags=1), UNS),
+    (dict(rel_idx=A + 2), UNS),
 ])
 def test_padded_rejections(kw, status):
     assert padded(**kw) == status
@@ -104,6 +105,7 @@ def test_flags0_needs_no_relative_tables():
     (dict(cu=None), INV), (dict(nseq=-1), INV), (dict(total=-1), INV), (dict(max_seqlen=-1), INV),
     (dict(rel_max_len=100), INV), (dict(max_seqlen=9000, rel_max_len=9000), UNS), (dict(q=None), INV),
     (dict(d=16), UNS), (dict(k=MIS), UNS), (dict(n_rel=1 << 20, ld_rel=1 << 10), UNS),
+    (dict(cu=A + 2), UNS),
 ])
 def test_varlen_rejections(kw, status):
     assert varlen(**kw) == status
@@ -117,6 +119,7 @@ def test_varlen_empty_is_noop(kw):
 @pytest.mark.parametrize("args,status", [
     ((None, 10, 256, 512), INV), ((A, 0, 256, 512), INV), ((A, 10, 1, 512), INV),
     ((A, 10, 256, 129), INV), ((A, 10, 0, 0), INV), ((A, 70000, 256, 512), UNS),
+    ((A + 2, 10, 256, 512), UNS),
 ])
 def test_rel_bucket_rejections(args, status):
     assert dd.lib().rel_bucket(*args, None) == status
@@ -132,6 +135,7 @@ def pack_index(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(B=-1), INV), (dict(L=-1), INV), (dict(cu=None), INV), (dict(token_rows=None), INV),
     (dict(row_to_packed=None), INV), (dict(B=1 << 16, L=1 << 16), UNS),
+    (dict(cu=A + 2), UNS), (dict(token_rows=A + 1), UNS), (dict(max_seqlen=A + 2), UNS),
 ])
 def test_pack_index_rejections(kw, status):
     assert pack_index(**kw) == status
@@ -151,6 +155,7 @@ def rows(fn, **kw):
     (dict(ld_src=3056), INV), (dict(ld_dst=3056), INV),
     (dict(row_bytes=3064, ld_src=3072, ld_dst=3072), UNS), (dict(ld_src=3080), UNS),
     (dict(ld_dst=3080), UNS), (dict(src=MIS), UNS), (dict(dst=MIS), UNS),
+    (dict(index=A + 2), UNS),
 ])
 def test_row_copy_rejections(fn, kw, status):
     assert rows(fn, **kw) == status
