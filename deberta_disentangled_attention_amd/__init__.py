@@ -52,6 +52,12 @@ def lib() -> ctypes.CDLL:
         h.dattn_fwd_varlen.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, i64, i32, vp, i32,
                                        vp, i32, i32, i64, vp, i32, i32, i32, u32, f32, vp]
         h.dattn_fwd_varlen.restype = ctypes.c_int
+        h.dattn_fwd_padded_lse.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, i64, i32, vp, i32,
+                                           vp, vp, vp, i32, i32, i32, i32, i32, u32, f32, vp]
+        h.dattn_fwd_padded_lse.restype = ctypes.c_int
+        h.dattn_fwd_varlen_lse.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, i64, i32, vp, i32,
+                                           vp, i32, i32, i64, vp, vp, i32, i32, i32, u32, f32, vp]
+        h.dattn_fwd_varlen_lse.restype = ctypes.c_int
         h.dattn_pack_index.argtypes = [vp, i32, i32, vp, vp, vp, vp, vp]
         h.dattn_pack_index.restype = ctypes.c_int
         for fn in (h.dattn_pack_rows, h.dattn_unpack_rows):
@@ -110,10 +116,22 @@ def rel_bucket(max_len: int, position_buckets: int, max_relative_positions: int,
     return out
 
 
+def _lse_tensor(lse, rows: int, H: int, device):
+    import torch
+    if lse is True:
+        return torch.empty((rows, H), dtype=torch.float32, device=device)
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != rows * H:
+        raise ValueError("lse must be a contiguous float32 tensor of rows * H entries")
+    return lse
+
+
 def dattn_fwd_padded(q, k, v, qr, kr, rel_idx, rel_max_len: int, mask, H: int, d: int,
-                     *, flags: int = DATTN_C2P | DATTN_P2C, scale: float = 0.0, out=None):
+                     *, flags: int = DATTN_C2P | DATTN_P2C, scale: float = 0.0, out=None,
+                     lse=None):
     """Forward over a padded batch; q, k, v are [B, L, >=H*d] (views of a
-    fused QKV buffer are fine), mask is [B, L] uint8/bool or None."""
+    fused QKV buffer are fine), mask is [B, L] uint8/bool or None. With lse
+    (True, or a float32 [B*L, H] tensor) also returns each row's log-sum-exp:
+    (out, lse)."""
     import torch
     B, L = q.shape[0], q.shape[1]
     for name, t in (("k", k), ("v", v)):
@@ -136,20 +154,29 @@ def dattn_fwd_padded(q, k, v, qr, kr, rel_idx, rel_max_len: int, mask, H: int, d
     if out is None:
         out = torch.empty((B, L, H * d), dtype=q.dtype, device=q.device)
     n_rel = qr.shape[0] if qr is not None else 0
-    st = lib().dattn_fwd_padded(
+    if lse is None:
+        st = lib().dattn_fwd_padded(
+            _ptr(q), _ptr(k), _ptr(v), ld_q, ld_k, ld_v, _ptr(qr), _ptr(kr), ld_rel, n_rel,
+            _ptr(rel_idx), int(rel_max_len), _ptr(mask), _ptr(out), B, L, H, d,
+            _dtype_code(q), int(flags), float(scale), _stream(q))
+        _check(st, "dattn_fwd_padded")
+        return out
+    lse = _lse_tensor(lse, B * L, H, q.device)
+    st = lib().dattn_fwd_padded_lse(
         _ptr(q), _ptr(k), _ptr(v), ld_q, ld_k, ld_v, _ptr(qr), _ptr(kr), ld_rel, n_rel,
-        _ptr(rel_idx), int(rel_max_len), _ptr(mask), _ptr(out), B, L, H, d,
+        _ptr(rel_idx), int(rel_max_len), _ptr(mask), _ptr(out), _ptr(lse), B, L, H, d,
         _dtype_code(q), int(flags), float(scale), _stream(q))
-    _check(st, "dattn_fwd_padded")
-    return out
+    _check(st, "dattn_fwd_padded_lse")
+    return out, lse
 
 
 def dattn_fwd_varlen(q, k, v, qr, kr, rel_idx, rel_max_len: int, cu_seqlens, max_seqlen: int,
                      H: int, d: int, *, flags: int = DATTN_C2P | DATTN_P2C, scale: float = 0.0,
-                     out=None, total_tokens: Optional[int] = None):
+                     out=None, total_tokens: Optional[int] = None, lse=None):
     """Forward over packed sequences; q, k, v are [total_tokens, >=H*d] and
     cu_seqlens a device int32 [nseq+1]. max_seqlen (and total_tokens, by
-    default q.shape[0]) are host values."""
+    default q.shape[0]) are host values. With lse (True, or a float32
+    [total_tokens, H] tensor) also returns each row's log-sum-exp."""
     import torch
     T = q.shape[0] if total_tokens is None else int(total_tokens)
     ld_q, ld_k, ld_v = _row_stride(q, "q"), _row_stride(k, "k"), _row_stride(v, "v")
@@ -163,13 +190,22 @@ def dattn_fwd_varlen(q, k, v, qr, kr, rel_idx, rel_max_len: int, cu_seqlens, max
     if out is None:
         out = torch.empty((q.shape[0], H * d), dtype=q.dtype, device=q.device)
     n_rel = qr.shape[0] if qr is not None else 0
-    st = lib().dattn_fwd_varlen(
+    if lse is None:
+        st = lib().dattn_fwd_varlen(
+            _ptr(q), _ptr(k), _ptr(v), ld_q, ld_k, ld_v, _ptr(qr), _ptr(kr), ld_rel, n_rel,
+            _ptr(rel_idx), int(rel_max_len), _ptr(cu_seqlens), cu_seqlens.numel() - 1,
+            int(max_seqlen), T, _ptr(out), H, d, _dtype_code(q), int(flags), float(scale),
+            _stream(q))
+        _check(st, "dattn_fwd_varlen")
+        return out
+    lse = _lse_tensor(lse, q.shape[0], H, q.device)
+    st = lib().dattn_fwd_varlen_lse(
         _ptr(q), _ptr(k), _ptr(v), ld_q, ld_k, ld_v, _ptr(qr), _ptr(kr), ld_rel, n_rel,
         _ptr(rel_idx), int(rel_max_len), _ptr(cu_seqlens), cu_seqlens.numel() - 1,
-        int(max_seqlen), T, _ptr(out), H, d, _dtype_code(q), int(flags), float(scale),
-        _stream(q))
-    _check(st, "dattn_fwd_varlen")
-    return out
+        int(max_seqlen), T, _ptr(out), _ptr(lse), H, d, _dtype_code(q), int(flags),
+        float(scale), _stream(q))
+    _check(st, "dattn_fwd_varlen_lse")
+    return out, lse
 
 
 def pack_index(mask, B: Optional[int] = None, L: Optional[int] = None, *, device=None):

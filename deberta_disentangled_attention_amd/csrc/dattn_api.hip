@@ -70,12 +70,13 @@ int rel_bucket(int32_t* rel_idx, int32_t max_len, int32_t position_buckets,
   return dattn::launch_rel_bucket(rel_idx, max_len, position_buckets, max_relative_positions, stream);
 }
 
-int dattn_fwd_padded(const void* q, const void* k, const void* v, int64_t ld_q, int64_t ld_k,
-                     int64_t ld_v, const void* qr, const void* kr, int64_t ld_rel, int32_t n_rel,
-                     const int32_t* rel_idx, int32_t rel_max_len, const uint8_t* mask, void* out,
-                     int32_t B, int32_t L, int32_t H, int32_t d, int32_t dtype, uint32_t flags,
-                     float scale, hipStream_t stream) {
+static int fwd_padded(const void* q, const void* k, const void* v, int64_t ld_q, int64_t ld_k,
+                      int64_t ld_v, const void* qr, const void* kr, int64_t ld_rel, int32_t n_rel,
+                      const int32_t* rel_idx, int32_t rel_max_len, const uint8_t* mask, void* out,
+                      int32_t B, int32_t L, int32_t H, int32_t d, int32_t dtype, uint32_t flags,
+                      float scale, float* lse, hipStream_t stream) {
   if (B < 0 || L < 0) return DATTN_ERR_INVALID_ARGUMENT;
+  if (!aligned4(lse)) return DATTN_ERR_UNSUPPORTED;
   int st = check_common(q, k, v, ld_q, ld_k, ld_v, qr, kr, ld_rel, n_rel, rel_idx, rel_max_len,
                         out, H, d, dtype, flags, scale, L);
   if (st != DATTN_OK) return st;
@@ -89,15 +90,18 @@ int dattn_fwd_padded(const void* q, const void* k, const void* v, int64_t ld_q, 
   p.cu_seqlens = nullptr; p.nseq = 0; p.total_tokens = (int64_t)B * L;
   p.out = out; p.H = H; p.flags = flags;
   p.scale_log2 = scale_log2(d, flags, scale);
+  p.lse = lse;
   return dattn::launch_fwd(p, dtype, d, false, stream);
 }
 
-int dattn_fwd_varlen(const void* q, const void* k, const void* v, int64_t ld_q, int64_t ld_k,
-                     int64_t ld_v, const void* qr, const void* kr, int64_t ld_rel, int32_t n_rel,
-                     const int32_t* rel_idx, int32_t rel_max_len, const int32_t* cu_seqlens,
-                     int32_t nseq, int32_t max_seqlen, int64_t total_tokens, void* out, int32_t H,
-                     int32_t d, int32_t dtype, uint32_t flags, float scale, hipStream_t stream) {
+static int fwd_varlen(const void* q, const void* k, const void* v, int64_t ld_q, int64_t ld_k,
+                      int64_t ld_v, const void* qr, const void* kr, int64_t ld_rel, int32_t n_rel,
+                      const int32_t* rel_idx, int32_t rel_max_len, const int32_t* cu_seqlens,
+                      int32_t nseq, int32_t max_seqlen, int64_t total_tokens, void* out, int32_t H,
+                      int32_t d, int32_t dtype, uint32_t flags, float scale, float* lse,
+                      hipStream_t stream) {
   if (nseq < 0 || total_tokens < 0 || max_seqlen < 0) return DATTN_ERR_INVALID_ARGUMENT;
+  if (!aligned4(lse)) return DATTN_ERR_UNSUPPORTED;
   if (!cu_seqlens) return DATTN_ERR_INVALID_ARGUMENT;
   if (!aligned4(cu_seqlens)) return DATTN_ERR_UNSUPPORTED;
   int st = check_common(q, k, v, ld_q, ld_k, ld_v, qr, kr, ld_rel, n_rel, rel_idx, rel_max_len,
@@ -113,7 +117,50 @@ int dattn_fwd_varlen(const void* q, const void* k, const void* v, int64_t ld_q, 
   p.cu_seqlens = cu_seqlens; p.nseq = nseq; p.total_tokens = total_tokens;
   p.out = out; p.H = H; p.flags = flags;
   p.scale_log2 = scale_log2(d, flags, scale);
+  p.lse = lse;
   return dattn::launch_fwd(p, dtype, d, true, stream);
+}
+
+int dattn_fwd_padded(const void* q, const void* k, const void* v, int64_t ld_q, int64_t ld_k,
+                     int64_t ld_v, const void* qr, const void* kr, int64_t ld_rel, int32_t n_rel,
+                     const int32_t* rel_idx, int32_t rel_max_len, const uint8_t* mask, void* out,
+                     int32_t B, int32_t L, int32_t H, int32_t d, int32_t dtype, uint32_t flags,
+                     float scale, hipStream_t stream) {
+  return fwd_padded(q, k, v, ld_q, ld_k, ld_v, qr, kr, ld_rel, n_rel, rel_idx, rel_max_len, mask,
+                    out, B, L, H, d, dtype, flags, scale, nullptr, stream);
+}
+
+int dattn_fwd_padded_lse(const void* q, const void* k, const void* v, int64_t ld_q, int64_t ld_k,
+                         int64_t ld_v, const void* qr, const void* kr, int64_t ld_rel,
+                         int32_t n_rel, const int32_t* rel_idx, int32_t rel_max_len,
+                         const uint8_t* mask, void* out, float* lse, int32_t B, int32_t L,
+                         int32_t H, int32_t d, int32_t dtype, uint32_t flags, float scale,
+                         hipStream_t stream) {
+  if (!lse) return DATTN_ERR_INVALID_ARGUMENT;
+  return fwd_padded(q, k, v, ld_q, ld_k, ld_v, qr, kr, ld_rel, n_rel, rel_idx, rel_max_len, mask,
+                    out, B, L, H, d, dtype, flags, scale, lse, stream);
+}
+
+int dattn_fwd_varlen(const void* q, const void* k, const void* v, int64_t ld_q, int64_t ld_k,
+                     int64_t ld_v, const void* qr, const void* kr, int64_t ld_rel, int32_t n_rel,
+                     const int32_t* rel_idx, int32_t rel_max_len, const int32_t* cu_seqlens,
+                     int32_t nseq, int32_t max_seqlen, int64_t total_tokens, void* out, int32_t H,
+                     int32_t d, int32_t dtype, uint32_t flags, float scale, hipStream_t stream) {
+  return fwd_varlen(q, k, v, ld_q, ld_k, ld_v, qr, kr, ld_rel, n_rel, rel_idx, rel_max_len,
+                    cu_seqlens, nseq, max_seqlen, total_tokens, out, H, d, dtype, flags, scale,
+                    nullptr, stream);
+}
+
+int dattn_fwd_varlen_lse(const void* q, const void* k, const void* v, int64_t ld_q, int64_t ld_k,
+                         int64_t ld_v, const void* qr, const void* kr, int64_t ld_rel,
+                         int32_t n_rel, const int32_t* rel_idx, int32_t rel_max_len,
+                         const int32_t* cu_seqlens, int32_t nseq, int32_t max_seqlen,
+                         int64_t total_tokens, void* out, float* lse, int32_t H, int32_t d,
+                         int32_t dtype, uint32_t flags, float scale, hipStream_t stream) {
+  if (!lse) return DATTN_ERR_INVALID_ARGUMENT;
+  return fwd_varlen(q, k, v, ld_q, ld_k, ld_v, qr, kr, ld_rel, n_rel, rel_idx, rel_max_len,
+                    cu_seqlens, nseq, max_seqlen, total_tokens, out, H, d, dtype, flags, scale,
+                    lse, stream);
 }
 
 int dattn_pack_index(const uint8_t* mask, int32_t B, int32_t L, int32_t* cu_seqlens,

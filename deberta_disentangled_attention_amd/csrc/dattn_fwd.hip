@@ -475,6 +475,8 @@ void dattn_fwd_kernel(FwdParams p) {
         const int64_t off = ((base + r0 + r) * (int64_t)p.H * D + (int64_t)head * D) * ES + 16 * u;
         *reinterpret_cast<uint4*>(o + off) = make_uint4(0, 0, 0, 0);
       }
+      if (p.lse)
+        for (int r = tid; r < nrow; r += NT) p.lse[(base + r0 + r) * p.H + head] = NEG_INF;
       return;
     }
   } else {
@@ -1583,6 +1585,10 @@ void dattn_fwd_kernel(FwdParams p) {
     bool row_ok = qi < ext && l_tot > 0.f;
     if (!VARLEN && mrow && qi < ext) row_ok = row_ok && mrow[qi] != 0;
     const float inv = row_ok ? 1.f / l_tot : 0.f;
+    // log of the row's sum of exp(tau S): the exponentials were taken as
+    // exp2(tau log2(e) S - m_run), so it is ln 2 (m_run + log2 l)
+    if (p.lse && lh == 0 && qi < row_limit)
+      p.lse[(base + qi) * p.H + head] = row_ok ? (m_run + log2f(l_tot)) * 0.6931471805599453f : NEG_INF;
     if (qi < row_limit) {
       unsigned char* o = reinterpret_cast<unsigned char*>(p.out) +
                          ((base + qi) * (int64_t)p.H * D + hoff) * ES;

@@ -31,6 +31,7 @@ struct FwdParams {
   int32_t H;
   uint32_t flags;
   float scale_log2;     // softmax scale times log2(e)
+  float* lse;           // [tokens, H] natural log of each row's sum of exp(scores), or null
   int32_t n_qtiles;     // padded: query tiles per sequence; packed: tile slots
   int32_t n_work;       // total workgroups launched
 };

@@ -152,6 +152,37 @@ int dattn_fwd_varlen(const void* q, const void* k, const void* v,
                      uint32_t flags, float scale, hipStream_t stream);
 
 /*
+ * dattn_fwd_padded_lse, dattn_fwd_varlen_lse - the same forwards, also
+ * writing each row's log-sum-exp, the statistic a backward pass or a merge
+ * of partial attentions reads:
+ *
+ *   lse[t * H + h] = ln sum_j exp(S_tj)   over the valid keys j of row t,
+ *
+ * with S the scaled scores above; -inf for rows with no valid key (padded
+ * queries, empty sequences). lse is a device float32 array of [B*L, H]
+ * (padded) or [total_tokens, H] (packed) entries, 4-byte aligned, written
+ * for every row the output covers. Other arguments, outputs and errors are
+ * those of dattn_fwd_padded / dattn_fwd_varlen; a NULL lse is
+ * INVALID_ARGUMENT.
+ */
+int dattn_fwd_padded_lse(const void* q, const void* k, const void* v,
+                         int64_t ld_q, int64_t ld_k, int64_t ld_v,
+                         const void* qr, const void* kr, int64_t ld_rel, int32_t n_rel,
+                         const int32_t* rel_idx, int32_t rel_max_len,
+                         const uint8_t* mask, void* out, float* lse,
+                         int32_t B, int32_t L, int32_t H, int32_t d, int32_t dtype,
+                         uint32_t flags, float scale, hipStream_t stream);
+
+int dattn_fwd_varlen_lse(const void* q, const void* k, const void* v,
+                         int64_t ld_q, int64_t ld_k, int64_t ld_v,
+                         const void* qr, const void* kr, int64_t ld_rel, int32_t n_rel,
+                         const int32_t* rel_idx, int32_t rel_max_len,
+                         const int32_t* cu_seqlens, int32_t nseq, int32_t max_seqlen,
+                         int64_t total_tokens, void* out, float* lse,
+                         int32_t H, int32_t d, int32_t dtype,
+                         uint32_t flags, float scale, hipStream_t stream);
+
+/*
  * dattn_rel_proj - the per-head relative tables from the relative embeddings:
  *
  *   qr = E Wq^T + bq,   kr = E Wk^T + bk

@@ -149,3 +149,25 @@ def dattn_varlen_bwd(q, k, v, qr, kr, rel_idx, rel_max_len: int, cu_seqlens, H: 
             g["dkr"][:, sl] += dKR
             g["lse"][lo:hi, h] = lse
     return g
+
+
+def lse_rows(q_seq, k_seq, qr, kr, rel_idx, rel_max_len: int, h: int, d: int, rows,
+             valid=None, flags: int = 3, scale: float = 0.0) -> np.ndarray:
+    """Row log-sum-exp (natural log) of selected rows of one (sequence,
+    head) unit, -inf for rows with no valid key or a padded query; for
+    checking sampled rows where the whole unit is too slow."""
+    L = k_seq.shape[0]
+    T = _check_table(rel_idx, rel_max_len, L, qr.shape[0])
+    tau = scale if scale > 0 else default_scale(d, flags)
+    rows = np.asarray(rows, dtype=np.int64)
+    S = unit_scores(_head(q_seq, h, d), _head(k_seq, h, d), _head(qr, h, d), _head(kr, h, d),
+                    T, rel_max_len, flags, tau, rows)
+    keys = np.ones(L, dtype=bool) if valid is None else np.asarray(valid).astype(bool)
+    out = np.full(len(rows), -np.inf)
+    if keys.any():
+        Sv = S[:, keys]
+        mx = Sv.max(axis=1)
+        out = mx + np.log(np.exp(Sv - mx[:, None]).sum(axis=1))
+        if valid is not None:
+            out = np.where(keys[rows], out, -np.inf)
+    return out

@@ -190,3 +190,31 @@ def test_rel_proj_rejections(kw, status):
 @pytest.mark.parametrize("kw", [dict(n_rel=0), dict(HD=0), dict(n_rel=0, E=None)])
 def test_rel_proj_empty_is_noop(kw):
     assert rel_proj(**kw) == dd.DATTN_OK
+
+
+def padded_lse(**kw):
+    a = dict(q=A, k=A, v=A, ld_q=768, ld_k=768, ld_v=768, qr=A, kr=A, ld_rel=768, n_rel=512,
+             rel_idx=A, rel_max_len=512, mask=None, out=A, lse=A, B=2, L=512, H=12, d=64,
+             dtype=2, flags=3, scale=0.0, stream=None)
+    a.update(kw)
+    return dd.lib().dattn_fwd_padded_lse(*a.values())
+
+
+def varlen_lse(**kw):
+    a = dict(q=A, k=A, v=A, ld_q=768, ld_k=768, ld_v=768, qr=A, kr=A, ld_rel=768, n_rel=512,
+             rel_idx=A, rel_max_len=512, cu=A, nseq=2, max_seqlen=512, total=1000, out=A,
+             lse=A, H=12, d=64, dtype=2, flags=3, scale=0.0, stream=None)
+    a.update(kw)
+    return dd.lib().dattn_fwd_varlen_lse(*a.values())
+
+
+@pytest.mark.parametrize("fn", [padded_lse, varlen_lse])
+@pytest.mark.parametrize("kw,status", [
+    (dict(lse=None), INV), (dict(lse=A + 2), UNS), (dict(q=None), INV), (dict(d=48), UNS),
+])
+def test_lse_rejections(fn, kw, status):
+    assert fn(**kw) == status
+
+
+def test_lse_empty_is_noop():
+    assert padded_lse(B=0) == dd.DATTN_OK and varlen_lse(nseq=0) == dd.DATTN_OK

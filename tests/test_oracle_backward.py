@@ -153,3 +153,15 @@ def test_varlen_equals_padded():
         assert np.allclose(gv[name], pk(gp[name]), atol=1e-13), name
     for name in ("dqr", "dkr"):
         assert np.allclose(gv[name], gp[name], atol=1e-12), name
+
+
+def test_lse_rows_matches_unit_backward():
+    q, k, v, qr, kr, T, m, dout = tiny(7)
+    g = BW.dattn_padded_bwd(q, k, v, qr, kr, T, 6, m, 2, 4, dout, 3)
+    for b in range(2):
+        for h in range(2):
+            got = BW.lse_rows(q[b], k[b], qr, kr, T, 6, h, 4, np.arange(6), valid=m[b])
+            want = g["lse"][b, :, h]
+            assert np.array_equal(np.isneginf(got), np.isneginf(want))
+            fin = np.isfinite(want)
+            assert np.allclose(got[fin], want[fin], rtol=0, atol=1e-12)
