@@ -1364,6 +1364,12 @@ void dattn_fwd_kernel(FwdParams p) {
           }
           __syncthreads();
         }
+        // the next general tile's K and V go to the other slot now, a whole
+        // tile ahead of their use (the slot's last reader, the previous
+        // tile, is past the barrier above); a wait for this tile's row
+        // loads also waits for these older loads, which costs less than
+        // exposing them at the next tile's start
+        if (tn >= 0) issue_tile(tn, ring + (par ^ 1) * C::SLOT_BYTES);
         m = uniform(m);
         const Modes mn = uniform(tn >= 0 ? wave_modes(tn) : Modes{TERM_OFF, TERM_OFF, 0, 0.f});
         if (m.p2c == TERM_CONST) {
@@ -1429,9 +1435,6 @@ void dattn_fwd_kernel(FwdParams p) {
             add_f(f0, f1, acc);
           }
           if (!eb && !fb) next_first();
-          // the next general tile's K and V, after every row fetch this tile
-          // consumes (a wait for those rows then never waits for these loads)
-          if (tn >= 0) issue_tile(tn, ring + (par ^ 1) * C::SLOT_BYTES);
           mask_keys(1, acc);
           s[1] = acc;
         }
