@@ -1,6 +1,7 @@
 /*
  * dattn.h - C ABI of libdattn.so, the disentangled-attention forward for
- * AMD Instinct MI355X (gfx950).
+ * AMD Instinct MI355X (gfx950), with the steps around it: the relative-row
+ * table, the per-head relative projections, and padded <-> packed rows.
  *
  * The operation is the exact, bidirectional DeBERTa-v2/v3 attention that
  * DisentangledFlash describes (README "Status": C2P/P2C disentangled
@@ -32,6 +33,8 @@
  *   - Row strides (ld_*) are in elements, must be >= H*d and a multiple of
  *     16 bytes; every array pointer must be 16-byte aligned. A fused QKV
  *     buffer [tokens, 3*H*d] is passed as three pointers with ld = 3*H*d.
+ *     The row-copy entries (dattn_pack_rows, dattn_unpack_rows) are the
+ *     exception: they move rows as bytes and take byte strides.
  *   - int32 arrays (tables, cu_seqlens, packing metadata) must be 4-byte
  *     aligned (UNSUPPORTED otherwise).
  *   - No hidden fallback: an unsupported case returns DATTN_ERR_UNSUPPORTED
