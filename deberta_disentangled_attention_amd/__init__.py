@@ -116,6 +116,33 @@ def rel_bucket(max_len: int, position_buckets: int, max_relative_positions: int,
     return out
 
 
+def _out_tensor(out, rows: int, width: int, like, lead=None):
+    """The caller's out, or a new one: a contiguous tensor of `rows` rows of
+    `width` elements with like's dtype and device (shape `lead` + [width]
+    when lead is given)."""
+    import torch
+    if out is None:
+        shape = (rows, width) if lead is None else (*lead, width)
+        return torch.empty(shape, dtype=like.dtype, device=like.device)
+    if (out.dtype != like.dtype or out.device != like.device or not out.is_contiguous()
+            or out.numel() != rows * width or (out.dim() and out.shape[-1] != width)):
+        raise ValueError(f"out must be a contiguous {like.dtype} tensor of {rows} rows of "
+                         f"{width} elements on {like.device}")
+    return out
+
+
+def _table_check(rel_idx, rel_max_len: int, flags: int, device) -> None:
+    import torch
+    if rel_idx is None:
+        if flags:
+            raise ValueError("rel_idx is required when a position term is enabled")
+        return
+    if (rel_idx.dtype != torch.int32 or not rel_idx.is_contiguous()
+            or rel_idx.numel() != 2 * int(rel_max_len) - 1 or rel_idx.device != device):
+        raise ValueError("rel_idx must be a contiguous int32 tensor of 2*rel_max_len-1 "
+                         "entries on the inputs' device")
+
+
 def _lse_tensor(lse, rows: int, H: int, device):
     import torch
     if lse is True:
@@ -151,8 +178,8 @@ def dattn_fwd_padded(q, k, v, qr, kr, rel_idx, rel_max_len: int, mask, H: int, d
             mask = mask.view(torch.uint8)
         if mask.dtype != torch.uint8 or not mask.is_contiguous() or tuple(mask.shape) != (B, L):
             raise ValueError("mask must be a contiguous [B, L] uint8/bool tensor")
-    if out is None:
-        out = torch.empty((B, L, H * d), dtype=q.dtype, device=q.device)
+    _table_check(rel_idx, rel_max_len, flags, q.device)
+    out = _out_tensor(out, B * L, H * d, q, lead=(B, L))
     n_rel = qr.shape[0] if qr is not None else 0
     if lse is None:
         st = lib().dattn_fwd_padded(
@@ -179,6 +206,11 @@ def dattn_fwd_varlen(q, k, v, qr, kr, rel_idx, rel_max_len: int, cu_seqlens, max
     [total_tokens, H] tensor) also returns each row's log-sum-exp."""
     import torch
     T = q.shape[0] if total_tokens is None else int(total_tokens)
+    if T > q.shape[0] or T > k.shape[0] or T > v.shape[0]:
+        raise ValueError("total_tokens exceeds the rows of q, k or v")
+    for name, t in (("k", k), ("v", v)):
+        if t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{name} must match q in dtype and device")
     ld_q, ld_k, ld_v = _row_stride(q, "q"), _row_stride(k, "k"), _row_stride(v, "v")
     if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_contiguous():
         raise ValueError("cu_seqlens must be a contiguous int32 tensor")
@@ -187,8 +219,8 @@ def dattn_fwd_varlen(q, k, v, qr, kr, rel_idx, rel_max_len: int, cu_seqlens, max
         if kr is None or kr.stride() != qr.stride() or kr.shape != qr.shape:
             raise ValueError("qr and kr must have the same shape and strides")
         ld_rel = _row_stride(qr, "qr")
-    if out is None:
-        out = torch.empty((q.shape[0], H * d), dtype=q.dtype, device=q.device)
+    _table_check(rel_idx, rel_max_len, flags, q.device)
+    out = _out_tensor(out, T, H * d, q)
     n_rel = qr.shape[0] if qr is not None else 0
     if lse is None:
         st = lib().dattn_fwd_varlen(
@@ -198,7 +230,7 @@ def dattn_fwd_varlen(q, k, v, qr, kr, rel_idx, rel_max_len: int, cu_seqlens, max
             _stream(q))
         _check(st, "dattn_fwd_varlen")
         return out
-    lse = _lse_tensor(lse, q.shape[0], H, q.device)
+    lse = _lse_tensor(lse, T, H, q.device)
     st = lib().dattn_fwd_varlen_lse(
         _ptr(q), _ptr(k), _ptr(v), ld_q, ld_k, ld_v, _ptr(qr), _ptr(kr), ld_rel, n_rel,
         _ptr(rel_idx), int(rel_max_len), _ptr(cu_seqlens), cu_seqlens.numel() - 1,

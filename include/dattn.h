@@ -99,9 +99,13 @@ int rel_bucket(int32_t* rel_idx, int32_t max_len, int32_t position_buckets,
  *           batch b starts at element b*L*ld.
  * qr, kr  : [n_rel, >=H*d] projected relative tables, row stride ld_rel,
  *           shared by the whole batch. May be NULL when flags == 0.
- * rel_idx : the table from rel_bucket() for max_len = rel_max_len; needs
- *           rel_max_len >= L. Entries must lie in [0, n_rel); reads are
- *           clamped into that range. May be NULL when flags == 0.
+ * rel_idx : int32[2*rel_max_len - 1], the table from rel_bucket() for
+ *           max_len = rel_max_len; needs rel_max_len >= L. The entries
+ *           must be non-decreasing in the distance, as rel_bucket writes
+ *           them (the kernels find the table's two saturation distances by
+ *           search; other tables give undefined results). An entry outside
+ *           [0, n_rel) reads the nearest edge row: below 0 row 0, at or
+ *           above n_rel row n_rel - 1. May be NULL when flags == 0.
  * mask    : [B, L] bytes, nonzero = valid token, or NULL (all valid). It is
  *           the factorised 2-D mask m_i * m_j: a valid query attends to the
  *           valid keys only; positions are padded-row indices.
@@ -235,7 +239,10 @@ int dattn_rel_proj(const void* E, int64_t ld_e, const void* Wq, const void* Wk, 
  * row_to_packed : device int32[B * L], written: the packed index of padded
  *                 row i, or -1 where the mask is zero.
  * max_seqlen    : device int32[1] written with the longest row, or NULL.
- * Work is three launches on `stream`; nothing is read back to the host, so
+ * Work is one launch on `stream` for B <= 4096 rows and B*L <= 2^18
+ * tokens (one workgroup builds the whole index), three launches above
+ * that (per-row ranks, a scan, the placement); nothing is read back to the
+ * host, so
  * a caller that needs cu[B] (to size the packed buffers) or max_seqlen on
  * the host copies them itself. L is always a valid max_seqlen bound.
  *

@@ -114,23 +114,31 @@ def unit_forward(Qh, Kh, Vh, QRh, KRh, T, rel_max_len, valid, flags, tau,
     return masked_softmax_apply(S, Vh, valid[row_ids], valid)
 
 
-def _check_table(T: np.ndarray, rel_max_len: int, L: int, n_rel: int) -> np.ndarray:
+def _check_table(T: np.ndarray, rel_max_len: int, L: int, n_rel: int,
+                 clamp_rows: bool = False) -> np.ndarray:
+    """The relative-row table as int64. Rows outside [0, n_rel) are an error,
+    or, with clamp_rows, read as the nearest edge row (the library's
+    contract for such tables: a row index below 0 reads row 0, one at or
+    above n_rel reads row n_rel - 1)."""
     T = np.asarray(T, dtype=np.int64)
     if rel_max_len < L:
         raise ValueError("rel_max_len must cover the sequence length")
     if T.shape[0] != 2 * rel_max_len - 1:
         raise ValueError("table must have 2*rel_max_len-1 entries")
+    if clamp_rows:
+        return np.clip(T, 0, n_rel - 1)
     if T.min(initial=0) < 0 or T.max(initial=0) >= n_rel:
         raise ValueError("table rows outside the relative tables")
     return T
 
 
 def dattn_padded(q, k, v, qr, kr, rel_idx, rel_max_len: int, mask, H: int, d: int,
-                 flags: int = 3, scale: float = 0.0) -> np.ndarray:
+                 flags: int = 3, scale: float = 0.0, clamp_rows: bool = False) -> np.ndarray:
     """Padded layout. q, k, v: [B, L, H*d]; qr, kr: [n_rel, H*d]; mask:
-    [B, L] (1 = valid) or None. Returns float64 [B, L, H*d]."""
+    [B, L] (1 = valid) or None. Returns float64 [B, L, H*d]. clamp_rows:
+    see _check_table."""
     B, L, _ = q.shape
-    T = _check_table(rel_idx, rel_max_len, L, qr.shape[0])
+    T = _check_table(rel_idx, rel_max_len, L, qr.shape[0], clamp_rows)
     tau = scale if scale > 0 else default_scale(d, flags)
     out = np.zeros((B, L, H * d), dtype=np.float64)
     for b in range(B):
@@ -143,13 +151,14 @@ def dattn_padded(q, k, v, qr, kr, rel_idx, rel_max_len: int, mask, H: int, d: in
 
 
 def dattn_varlen(q, k, v, qr, kr, rel_idx, rel_max_len: int, cu_seqlens, H: int,
-                 d: int, flags: int = 3, scale: float = 0.0) -> np.ndarray:
+                 d: int, flags: int = 3, scale: float = 0.0,
+                 clamp_rows: bool = False) -> np.ndarray:
     """Packed layout. q, k, v: [total_tokens, H*d]; cu_seqlens: [nseq+1].
     Each sequence is one padded row of its own length with every token
     valid. Returns float64 [total_tokens, H*d]."""
     cu = np.asarray(cu_seqlens, dtype=np.int64)
     max_len = int(np.max(np.diff(cu))) if len(cu) > 1 else 0
-    T = _check_table(rel_idx, rel_max_len, max_len, qr.shape[0])
+    T = _check_table(rel_idx, rel_max_len, max_len, qr.shape[0], clamp_rows)
     tau = scale if scale > 0 else default_scale(d, flags)
     out = np.zeros((q.shape[0], H * d), dtype=np.float64)
     for b in range(len(cu) - 1):

@@ -32,33 +32,38 @@ def gpu_table(max_len, P, M):
 
 
 def run_padded(w: workloads.Workload, rel_max_len=None, flags=None, scale=0.0, mask=None,
-               q=None, k=None, v=None):
+               q=None, k=None, v=None, lse=None, table=None):
+    """The padded forward of w on the GPU; `table` (host int array) replaces
+    the rel_bucket table."""
     import torch
     import deberta_disentangled_attention_amd as dd
     rel_max_len = rel_max_len or w.L
     flags = w.flags if flags is None else flags
-    T = gpu_table(rel_max_len, w.position_buckets, w.max_relative_positions)
+    T = (gpu_table(rel_max_len, w.position_buckets, w.max_relative_positions) if table is None
+         else torch.from_numpy(np.ascontiguousarray(table, np.int32)).cuda())
     mask = w.mask if mask is None else mask
     m = None if mask is None else torch.from_numpy(np.ascontiguousarray(mask, np.uint8)).cuda()
     out = dd.dattn_fwd_padded(q if q is not None else dev(w.q, w.dtype),
                               k if k is not None else dev(w.k, w.dtype),
                               v if v is not None else dev(w.v, w.dtype),
                               dev(w.qr, w.dtype), dev(w.kr, w.dtype), T, rel_max_len, m,
-                              w.H, w.d, flags=flags, scale=scale)
+                              w.H, w.d, flags=flags, scale=scale, lse=lse)
     torch.cuda.synchronize()
     return out
 
 
-def run_varlen(w: workloads.Workload, rel_max_len=None, flags=None, scale=0.0):
+def run_varlen(w: workloads.Workload, rel_max_len=None, flags=None, scale=0.0, lse=None,
+               table=None):
     import torch
     import deberta_disentangled_attention_amd as dd
     rel_max_len = rel_max_len or max(w.max_seqlen, 1)
     flags = w.flags if flags is None else flags
-    T = gpu_table(rel_max_len, w.position_buckets, w.max_relative_positions)
+    T = (gpu_table(rel_max_len, w.position_buckets, w.max_relative_positions) if table is None
+         else torch.from_numpy(np.ascontiguousarray(table, np.int32)).cuda())
     cu = torch.from_numpy(w.cu_seqlens).cuda()
     out = dd.dattn_fwd_varlen(dev(w.q, w.dtype), dev(w.k, w.dtype), dev(w.v, w.dtype),
                               dev(w.qr, w.dtype), dev(w.kr, w.dtype), T, rel_max_len, cu,
-                              w.max_seqlen, w.H, w.d, flags=flags, scale=scale)
+                              w.max_seqlen, w.H, w.d, flags=flags, scale=scale, lse=lse)
     torch.cuda.synchronize()
     return out
 

@@ -218,3 +218,48 @@ def test_lse_rejections(fn, kw, status):
 
 def test_lse_empty_is_noop():
     assert padded_lse(B=0) == dd.DATTN_OK and varlen_lse(nseq=0) == dd.DATTN_OK
+
+
+# ---------------------------------------------------------------------------
+# the Python binding rejects buffers the kernels would overrun (CPU tensors:
+# every check runs before the library is called)
+# ---------------------------------------------------------------------------
+
+def _cpu_inputs(B=2, L=16, H=2, d=32, n_rel=8, dtype="float16"):
+    import torch
+    t = getattr(torch, dtype)
+    q = torch.zeros(B, L, H * d, dtype=t)
+    qr = torch.zeros(n_rel, H * d, dtype=t)
+    table = torch.zeros(2 * L - 1, dtype=torch.int32)
+    return q, qr, table
+
+
+@pytest.mark.parametrize("bad", ["shape", "dtype", "strided"])
+def test_binding_rejects_bad_out_padded(bad):
+    import torch
+    q, qr, table = _cpu_inputs()
+    out = {"shape": torch.zeros(2, 16, 32, dtype=torch.float16),
+           "dtype": torch.zeros(2, 16, 64, dtype=torch.float32),
+           "strided": torch.zeros(2, 16, 128, dtype=torch.float16)[..., :64]}[bad]
+    with pytest.raises(ValueError, match="out must be"):
+        dd.dattn_fwd_padded(q, q, q, qr, qr, table, 16, None, 2, 32, out=out)
+
+
+def test_binding_rejects_bad_table_and_tokens_varlen():
+    import torch
+    q, qr, table = _cpu_inputs()
+    qp = q.reshape(-1, q.shape[-1])
+    cu = torch.tensor([0, 16, 32], dtype=torch.int32)
+    with pytest.raises(ValueError, match="total_tokens exceeds"):
+        dd.dattn_fwd_varlen(qp, qp, qp, qr, qr, table, 16, cu, 16, 2, 32, total_tokens=33)
+    with pytest.raises(ValueError, match="rel_idx must be"):
+        dd.dattn_fwd_varlen(qp, qp, qp, qr, qr, table[:-1], 16, cu, 16, 2, 32)
+    with pytest.raises(ValueError, match="rel_idx must be"):
+        dd.dattn_fwd_varlen(qp, qp, qp, qr, qr, table.to(torch.int64), 16, cu, 16, 2, 32)
+    with pytest.raises(ValueError, match="rel_idx is required"):
+        dd.dattn_fwd_varlen(qp, qp, qp, qr, qr, None, 16, cu, 16, 2, 32)
+    with pytest.raises(ValueError, match="out must be"):
+        dd.dattn_fwd_varlen(qp, qp, qp, qr, qr, table, 16, cu, 16, 2, 32,
+                            out=torch.zeros(31, 64, dtype=torch.float16))
+    with pytest.raises(ValueError, match="k must match"):
+        dd.dattn_fwd_varlen(qp, qp.float(), qp, qr, qr, table, 16, cu, 16, 2, 32)

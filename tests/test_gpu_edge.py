@@ -225,3 +225,55 @@ def test_table_saturation_thresholds_across_lengths(L):
         got = H.host(H.run_padded(w))
         want = H.oracle_padded(w)
         H.assert_padded_close(got, want, H.valid_rows_padded(w), "fp32", f"sat L={L} P={P}")
+
+
+# ---------------------------------------------------------------------------
+# relative tables: windows too wide to stage, out-of-range rows
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("P,M,L", [(0, 1100, 2500), (512, 2048, 3000)])
+def test_wide_table_window_reads_table_from_memory(dtype, P, M, L):
+    """Tables whose non-saturated window spans more than the 2048 entries a
+    workgroup stages in LDS (identity span 1100; log buckets 512/2048):
+    band terms then read the table from device memory. Full check, padded
+    and packed."""
+    lens = np.array([L, L - 611])
+    w = workloads.make_workload(f"wide_{P}_{M}", dtype=dtype, B=2, L=L, H=1, d=64,
+                                position_buckets=P, max_relative_positions=M, lens=lens,
+                                seed=L + P)
+    T = oracle.rel_index_table(L, P, M)
+    lo = int(np.argmax(T != T[0])) - 1
+    hi = int(np.argmax(T == T[-1]))
+    assert hi - lo + 1 > 2048, (lo, hi)        # the window the kernel cannot stage
+    _say(f"wide table {dtype} P={P} M={M} L={L}")
+    got = H.host(H.run_padded(w))
+    want = H.oracle_padded(w)
+    worst = H.assert_padded_close(got, want, H.valid_rows_padded(w), dtype, "wide padded")
+    wp = workloads.to_packed(w)
+    gotp = H.host(H.run_varlen(wp, rel_max_len=L))
+    errp = float(np.abs(gotp - workloads.pack(want, w.lens)).max())
+    assert errp <= H.TOL[dtype], errp
+    _say(f"   max abs err padded {worst:.3e} packed {errp:.3e}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+def test_out_of_range_table_rows_read_edge_rows(dtype):
+    """A non-decreasing table whose entries run from -75 to 74 with only 40
+    rows in qr / kr: rows below 0 read row 0, rows from 40 on read row 39
+    (the oracle's clamp_rows reading)."""
+    L = 300
+    w = workloads.make_workload("clamp", dtype=dtype, B=2, L=L, H=2, d=64, position_buckets=20,
+                                max_relative_positions=64, lens=np.array([L, 123]), seed=17)
+    w.qr, w.kr = w.qr[:40].copy(), w.kr[:40].copy()
+    T = (np.arange(-(L - 1), L) // 4).astype(np.int32)
+    assert T.min() < 0 and T.max() >= 40
+    got = H.host(H.run_padded(w, table=T))
+    want = oracle.dattn_padded(w.q, w.k, w.v, w.qr, w.kr, T, L, w.mask, w.H, w.d,
+                               clamp_rows=True)
+    worst = H.assert_padded_close(got, want, H.valid_rows_padded(w), dtype, "clamp padded")
+    wp = workloads.to_packed(w)
+    gotp = H.host(H.run_varlen(wp, rel_max_len=L, table=T))
+    errp = float(np.abs(gotp - workloads.pack(want, w.lens)).max())
+    assert errp <= H.TOL[dtype], errp
+    _say(f"clamp {dtype}: max abs err padded {worst:.3e} packed {errp:.3e}")

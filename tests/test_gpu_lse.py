@@ -3,12 +3,14 @@ oracle (oracle.backward.lse_rows).
 
 Bar, absolute: 1e-5 (fp32), 5e-3 (fp16), 1e-2 (bf16). lse is the log of the
 row sum of exponentials, so a change of every score by at most e moves it by
-at most e; the row sum itself is taken from the exponentials before they
-are rounded, so the 16-bit bars are those of the scores: products of inputs
-in the element type accumulated in fp32, and on far tiles the operand
-q_i + qr[row] rounded once (relative 2^-9 bf16, 2^-11 fp16). Rows without a
-valid key must be -inf, and the output must be bit-identical to the forward
-without lse.
+at most e. The scores carry the products of inputs in the element type
+accumulated in fp32 and, on far tiles, the operand q_i + qr[row] rounded
+once (relative 2^-9 bf16, 2^-11 fp16). For the 16-bit types the row sum is
+taken from the exponentials after they are rounded to the element type (the
+same P the P.V product reads), each term off by at most that relative
+amount, which moves the log of the sum by at most 2^-9 (bf16) or 2^-11
+(fp16). Rows without a valid key must be -inf, and the output must be
+bit-identical to the forward without lse.
 """
 
 import sys
@@ -16,8 +18,10 @@ import sys
 import numpy as np
 import pytest
 
+import oracle
 import workloads
 from oracle import backward as BW
+from tests import dense
 from tests import helpers as H
 
 pytestmark = pytest.mark.gpu
@@ -101,26 +105,22 @@ def test_lse_varlen(dtype):
             _check(got[lo:hi, h], want, dtype, f"seq {b} h={h}")
 
 
-def test_lse_long_packed_sampled():
+def test_lse_long_packed_dense():
     """The benchmark workload (16 x 8192 packed bf16) in its launch
-    configuration, sampled rows."""
-    import torch
-    import deberta_disentangled_attention_amd as dd
+    configuration: covering rows of every (sequence, head) unit (every
+    workgroup and wave) and one whole unit."""
     w = workloads.c4_long_packed_bf16()
-    T = H.gpu_table(w.max_seqlen, w.position_buckets, w.max_relative_positions)
-    cu = torch.from_numpy(w.cu_seqlens).cuda()
-    _, lse = dd.dattn_fwd_varlen(H.dev(w.q, w.dtype), H.dev(w.k, w.dtype), H.dev(w.v, w.dtype),
-                                 H.dev(w.qr, w.dtype), H.dev(w.kr, w.dtype), T, w.max_seqlen, cu,
-                                 w.max_seqlen, w.H, w.d, lse=True)
-    torch.cuda.synchronize()
+    out0 = H.run_varlen(w)
+    out, lse = H.run_varlen(w, lse=True)
+    import torch
+    assert torch.equal(out, out0)
     got = lse.cpu().numpy().astype(np.float64)
-    Tn = np.asarray(T.cpu().numpy(), dtype=np.int64)
-    rng = np.random.default_rng(2)
-    worst = 0.0
-    for b in rng.choice(w.B, size=3, replace=False):
-        h = int(rng.integers(0, w.H))
-        lo, hi = int(w.cu_seqlens[b]), int(w.cu_seqlens[b + 1])
-        rows = np.unique(np.concatenate([[0, hi - lo - 1], rng.integers(0, hi - lo, size=6)]))
-        want = BW.lse_rows(w.q[lo:hi], w.k[lo:hi], w.qr, w.kr, Tn, w.max_seqlen, h, w.d, rows)
-        worst = max(worst, _check(got[lo + rows, h], want, w.dtype, f"c4 seq {b} h={h}"))
-    _say(f"c4 sampled lse max err {worst:.3e}")
+    T = oracle.rel_index_table(w.max_seqlen, w.position_buckets, w.max_relative_positions)
+    cu = w.cu_seqlens
+    units = [(b, h) for b in range(w.B) for h in range(w.H)]
+    jobs = dense.unit_jobs("lse", w, T, w.max_seqlen, units, full_units=[(7, 3)], seed=6)
+    worst, nrows = 0.0, 0
+    for (b, h), rows, want in dense.run_jobs(jobs):
+        worst = max(worst, _check(got[int(cu[b]) + rows, h], want, w.dtype, f"c4 seq {b} h={h}"))
+        nrows += len(rows)
+    _say(f"c4 dense lse: {nrows} rows checked, max err {worst:.3e}")

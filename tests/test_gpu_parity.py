@@ -14,6 +14,7 @@ import pytest
 
 import oracle
 import workloads
+from tests import dense
 from tests import helpers as H
 
 pytestmark = pytest.mark.gpu
@@ -140,49 +141,52 @@ def test_c3_padded_and_packed():
     _say(f"c3 max abs err padded {worst:.3e} packed {errp:.3e}")
 
 
-def _sampled_rows_check(w, got_fn, rows_per_unit=4, units=None, packed=True, seed=0):
-    rng = np.random.default_rng(seed)
-    T = oracle.rel_index_table(w.max_seqlen if packed else w.L, w.position_buckets,
-                               w.max_relative_positions)
-    relmax = w.max_seqlen if packed else w.L
-    cu = w.cu_seqlens
-    worst = 0.0
-    units = units or [(b, h) for b in range(w.B) for h in range(w.H)]
-    for (b, h) in units:
-        n = int(w.lens[b])
-        rows = np.unique(np.concatenate([[0, n - 1], rng.integers(0, n, size=rows_per_unit)]))
-        if packed:
-            sl = slice(int(cu[b]), int(cu[b + 1]))
-            qs, ks, vs = w.q[sl], w.k[sl], w.v[sl]
-        else:
-            qs, ks, vs = w.q[b], w.k[b], w.v[b]
-        want = oracle.dattn_rows(qs, ks, vs, w.qr, w.kr, T, relmax, h, w.d, rows,
-                                 flags=w.flags)
+def _dense_compare(jobs, got_fn, tol, tag):
+    """Run the oracle jobs and compare each with the GPU rows got_fn(b, h,
+    rows); returns the worst error and the number of rows checked."""
+    worst, nrows = 0.0, 0
+    for (b, h), rows, want in dense.run_jobs(jobs):
         got = got_fn(b, h, rows)
-        worst = max(worst, float(np.abs(got - want).max()))
-    assert worst <= H.TOL[w.dtype], worst
-    return worst
+        assert np.all(np.isfinite(got)), f"{tag}: non-finite output in unit {(b, h)}"
+        err = float(np.abs(got - want).max())
+        assert err <= tol, f"{tag}: unit {(b, h)} max abs err {err:.3e} > {tol:.1e}"
+        worst = max(worst, err)
+        nrows += len(rows)
+    return worst, nrows
 
 
-def test_c4_long_packed_sampled():
+def test_c4_long_packed_dense():
+    """The benchmark workload (16 x 8192 packed bf16, H=12) in the launch
+    configuration the benchmark times: covering rows of every (sequence,
+    head) unit -- every 128-query workgroup and every wave -- and two whole
+    units."""
     w = workloads.c4_long_packed_bf16()
     out = H.host(H.run_varlen(w))
     assert np.all(np.isfinite(out))
+    T = oracle.rel_index_table(w.max_seqlen, w.position_buckets, w.max_relative_positions)
     cu = w.cu_seqlens
-    rng = np.random.default_rng(1)
-    units = [(int(b), int(rng.integers(0, w.H))) for b in rng.choice(w.B, size=6, replace=False)]
-    worst = _sampled_rows_check(
-        w, lambda b, h, rows: out[int(cu[b]) + rows, h * w.d:(h + 1) * w.d], units=units)
-    _say(f"c4 sampled max abs err {worst:.3e}")
+    units = [(b, h) for b in range(w.B) for h in range(w.H)]
+    jobs = dense.unit_jobs("out", w, T, w.max_seqlen, units, full_units=[(0, 0), (15, 11)],
+                           seed=4)
+    worst, nrows = _dense_compare(
+        jobs, lambda b, h, rows: out[int(cu[b]) + rows, h * w.d:(h + 1) * w.d],
+        H.TOL[w.dtype], "c4")
+    _say(f"c4 dense: {len(units)} units, {nrows} rows checked, max abs err {worst:.3e}")
 
 
 @pytest.mark.parametrize("d,dtype", [(32, "bf16"), (128, "bf16"), (128, "fp32")])
 @pytest.mark.parametrize("flags", [3, 0])
-def test_c5_sweep_sampled(d, dtype, flags):
+def test_c5_sweep_dense(d, dtype, flags):
+    """Covering rows of every unit and one whole unit; the strict fp32
+    L=1024 case in full."""
     w = workloads.c5_sweep(d, dtype, flags)
     out = H.host(H.run_padded(w))
     assert np.all(np.isfinite(out))
-    units = [(0, 0), (1, 5), (3, 15)]
-    worst = _sampled_rows_check(w, lambda b, h, rows: out[b, rows, h * w.d:(h + 1) * w.d],
-                                units=units, packed=False)
-    _say(f"c5 d={d} {dtype} flags={flags} sampled max abs err {worst:.3e}")
+    T = oracle.rel_index_table(w.L, w.position_buckets, w.max_relative_positions)
+    units = [(b, h) for b in range(w.B) for h in range(w.H)]
+    full = units if dtype == "fp32" else [(1, 7)]
+    jobs = dense.unit_jobs("out", w, T, w.L, units, full_units=full, seed=5)
+    worst, nrows = _dense_compare(
+        jobs, lambda b, h, rows: out[b, rows, h * w.d:(h + 1) * w.d], H.TOL[w.dtype],
+        f"c5 d={d} {dtype} f{flags}")
+    _say(f"c5 d={d} {dtype} flags={flags}: {nrows} rows checked, max abs err {worst:.3e}")

@@ -264,3 +264,27 @@ def test_table_checks():
     T = bucket.rel_index_table(8, 8, 20)
     with pytest.raises(ValueError):
         oracle.dattn_padded(q, k, v, qr, kr, T, 8, None, 1, 4)   # rel_max_len < L
+
+
+@pytest.mark.parametrize("flags", [1, 2, 3])
+def test_clamp_rows_equals_tables_extended_by_their_edge_rows(flags):
+    """clamp_rows (a row index below 0 reads row 0, one at or above n_rel
+    reads row n_rel - 1) pinned against a different construction: the same
+    table shifted into range over qr / kr extended by copies of their first
+    and last rows; and also against the brute force."""
+    L, H, d, n_rel, pad = 11, 2, 4, 6, 9
+    q, k, v, _, _, mask = rand_case(21, 2, L, H, d, 3, 5)
+    rng = np.random.default_rng(3)
+    qr = rng.standard_normal((n_rel, H * d))
+    kr = rng.standard_normal((n_rel, H * d))
+    T = np.arange(-(L - 1), L) // 2 + 1            # -4 .. 6: both ends outside [0, 6)
+    assert T.min() < 0 and T.max() >= n_rel
+    with pytest.raises(ValueError):
+        oracle.dattn_padded(q, k, v, qr, kr, T, L, mask, H, d, flags)
+    got = oracle.dattn_padded(q, k, v, qr, kr, T, L, mask, H, d, flags, clamp_rows=True)
+    ext = lambda x: np.concatenate([np.repeat(x[:1], pad, 0), x, np.repeat(x[-1:], pad, 0)])
+    want = oracle.dattn_padded(q, k, v, ext(qr), ext(kr), T + pad, L, mask, H, d, flags)
+    assert np.allclose(got, want, rtol=0, atol=1e-12)
+    Tc = np.minimum(np.maximum(T, 0), n_rel - 1)
+    brute = brute_force(q, k, v, qr, kr, Tc, L, mask, H, d, flags, 0.0)
+    assert np.allclose(got, brute, rtol=0, atol=1e-12)
