@@ -59,6 +59,8 @@ def build_workload(name: str):
     import workloads
     table = {
         "c4": lambda: workloads.c4_long_packed_bf16(),
+        "c4l2048": lambda: workloads.c4_long_packed_bf16(nseq=64, seqlen=2048),
+        "c4l4096": lambda: workloads.c4_long_packed_bf16(nseq=32, seqlen=4096),
         "c2": lambda: workloads.c2_v3base_bf16(),
         "c3": lambda: workloads.c3_v2xlarge_fp16(),
         "c3p": lambda: workloads.c3_v2xlarge_fp16(packed=True),
@@ -70,6 +72,24 @@ def build_workload(name: str):
     if name not in table:
         raise SystemExit(f"unknown workload {name}; choose from {sorted(table)}")
     return table[name]()
+
+
+def algorithmic_bytes(w) -> float:
+    """HBM bytes the forward must move at least: Q, K, V read and O written
+    once per valid token and head (4 d esize), qr and kr read once per head
+    (2 n_rel d esize), and for the padded layout the zero rows of the
+    output, the mask and the relative-row table."""
+    import workloads
+    es = workloads.ESIZE[w.dtype]
+    b = 4.0 * w.d * es * w.H * w.total_tokens
+    if w.flags:
+        b += 2.0 * w.n_rel * w.d * es * w.H
+        b += 4.0 * (2 * (w.max_seqlen if w.packed else w.L) - 1)
+    if not w.packed:
+        b += (w.B * w.L - w.total_tokens) * w.H * w.d * es
+        if w.mask is not None:
+            b += w.B * w.L
+    return b
 
 
 def describe(w) -> str:
@@ -94,11 +114,23 @@ def _oracle_unit(args):
         return time.perf_counter() - t0
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, max_units: int) -> dict:
     import multiprocessing as mp
     import numpy as np
     import oracle
-    cores = min(len(os.sched_getaffinity(0)), max_units, 16)
+    host_cores = len(os.sched_getaffinity(0))
+    cores = min(host_cores, max_units)
     relmax = w.max_seqlen if w.packed else w.L
     T = oracle.rel_index_table(relmax, w.position_buckets, w.max_relative_positions)
     cu = w.cu_seqlens
@@ -121,10 +153,12 @@ def cpu_baseline(w, max_units: int) -> dict:
         pool.map(_oracle_unit, jobs, chunksize=1)
     wall = time.perf_counter() - t0
     return {"value": flop / wall / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{len(jobs)} whole (sequence, head) units of {describe(w).split(':')[0]} "
-                      f"({int(w.lens.max())} tokens each at most), float64 numpy oracle, one "
-                      f"single-threaded worker process per unit; wall {wall:.2f} s",
-            "wall_s": wall}
+            "sample": f"{len(jobs)} of the {w.B * w.H} whole (sequence, head) units of "
+                      f"{describe(w).split(':')[0]} ({int(w.lens.max())} tokens each at most), "
+                      f"float64 numpy oracle, one single-threaded worker process per unit on "
+                      f"{cores} of the {host_cores} host cores available; wall {wall:.2f} s",
+            "wall_s": wall, "host_cores": host_cores, "cpu_model": cpu_model(),
+            "units_timed": len(jobs), "units_total": w.B * w.H}
 
 
 # ---------------------------------------------------------------------------
@@ -329,8 +363,8 @@ def main():
         return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-units", type=int, default=16)
@@ -340,6 +374,9 @@ def main():
                     help="padded forward vs the device-packed route on a padded workload")
     ap.add_argument("--relproj", action="store_true",
                     help="time the qr/kr projection of the workload's table shape")
+    ap.add_argument("--flush-l2", action="store_true",
+                    help="overwrite a 512 MiB buffer before every step (outside the kernel's "
+                         "events) so inputs are not served from L2 / Infinity Cache")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -392,7 +429,12 @@ def main():
             dd.dattn_fwd_padded(q, k, v, qr, kr, table, relmax, mask, w.H, w.d,
                                 flags=w.flags, out=out)
 
+    flush_buf = (torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+                 if args.flush_l2 else None)
+
     def step(ev=None):
+        if flush_buf is not None:
+            flush_buf.fill_(1)
         dd.rel_bucket(relmax, w.position_buckets, w.max_relative_positions, out=table)
         if ev is not None:
             ev[0].record()
@@ -418,6 +460,13 @@ def main():
     total_ms = t0.elapsed_time(t1)
     kern_ms = [a.elapsed_time(b) for a, b in events]
     peak_extra = torch.cuda.max_memory_allocated() - base_mem
+    if flush_buf is not None:
+        peak_extra -= flush_buf.numel()
+    srt = sorted(kern_ms)
+
+    def pct(p):
+        # nearest-rank percentile of the per-launch kernel times
+        return srt[min(len(srt) - 1, max(0, int(math.ceil(p / 100.0 * len(srt))) - 1))]
 
     flop = w.effective_flop()
     ms_per_step = total_ms / args.steps
@@ -425,7 +474,7 @@ def main():
     value = flop / (ms_per_step * 1e-3) / 1e12
     achieved = flop / (kern_avg_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    traffic = load_traffic() if args.workload == "c4" else None
+    traffic = load_traffic() if (args.workload == "c4" and w.flags == 3) else None
     res = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -452,8 +501,13 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic,
                      "kernel": "dattn_fwd_kernel", "kernel_avg_ms": round(kern_avg_ms, 4),
+                     "kernel_median_ms": round(pct(50), 4),
+                     "kernel_p10_ms": round(pct(10), 4), "kernel_p90_ms": round(pct(90), 4),
                      "kernel_min_ms": round(min(kern_ms), 4),
-                     "kernel_max_ms": round(max(kern_ms), 4)},
+                     "kernel_max_ms": round(max(kern_ms), 4),
+                     "median_frac": round(flop / (pct(50) * 1e-3) / 1e12 / peak, 4),
+                     "hbm_GBps_algorithmic": round(algorithmic_bytes(w) / (kern_avg_ms * 1e-3) / 1e9, 1),
+                     "l2_flushed": bool(args.flush_l2)},
         "device_memory": {"peak_extra_bytes_during_steps": int(peak_extra),
                           "relative_table_bytes": int(table.numel() * 4)},
         "host_wall_s_timed_region": round(wall, 4),

@@ -60,6 +60,7 @@ int rel_bucket(int32_t* rel_idx, int32_t max_len, int32_t position_buckets,
   if (!rel_idx || max_len < 1) return DATTN_ERR_INVALID_ARGUMENT;
   if (!aligned4(rel_idx)) return DATTN_ERR_UNSUPPORTED;
   if (max_len > 65536) return DATTN_ERR_UNSUPPORTED;
+  if (position_buckets > 4096) return DATTN_ERR_UNSUPPORTED;
   if (position_buckets > 0) {
     const int mid = position_buckets / 2;
     if (mid < 1) return DATTN_ERR_INVALID_ARGUMENT;
@@ -86,7 +87,7 @@ static int fwd_padded(const void* q, const void* k, const void* v, int64_t ld_q,
   p.ld_q = ld_q; p.ld_k = ld_k; p.ld_v = ld_v;
   p.qr = qr; p.kr = kr; p.ld_rel = ld_rel; p.n_rel = n_rel;
   p.rel_idx = rel_idx; p.rel_max_len = rel_max_len;
-  p.mask = mask; p.B = B; p.L = L;
+  p.mask = mask; p.B = B; p.L = L; p.max_seqlen = L;
   p.cu_seqlens = nullptr; p.nseq = 0; p.total_tokens = (int64_t)B * L;
   p.out = out; p.H = H; p.flags = flags;
   p.scale_log2 = scale_log2(d, flags, scale);
@@ -113,7 +114,7 @@ static int fwd_varlen(const void* q, const void* k, const void* v, int64_t ld_q,
   p.ld_q = ld_q; p.ld_k = ld_k; p.ld_v = ld_v;
   p.qr = qr; p.kr = kr; p.ld_rel = ld_rel; p.n_rel = n_rel;
   p.rel_idx = rel_idx; p.rel_max_len = rel_max_len;
-  p.mask = nullptr; p.B = 0; p.L = 0;
+  p.mask = nullptr; p.B = 0; p.L = 0; p.max_seqlen = max_seqlen;
   p.cu_seqlens = cu_seqlens; p.nseq = nseq; p.total_tokens = total_tokens;
   p.out = out; p.H = H; p.flags = flags;
   p.scale_log2 = scale_log2(d, flags, scale);

@@ -32,6 +32,7 @@ struct FwdParams {
   uint32_t flags;
   float scale_log2;     // softmax scale times log2(e)
   float* lse;           // [tokens, H] natural log of each row's sum of exp(scores), or null
+  int32_t max_seqlen;   // padded: L; packed: the caller's bound on every length
   int32_t n_qtiles;     // padded: query tiles per sequence; packed: tile slots
   int32_t n_work;       // total workgroups launched
 };

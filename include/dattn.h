@@ -79,15 +79,20 @@ extern "C" {
  *       with M = max_relative_positions; s = position_buckets.
  *   position_buckets <= 0: no bucketing, b(r) = r, s = max_relative_positions.
  * The forward then reads 2s rows of qr and kr (n_rel = 2s).
- * The ceiling is of the real number: the kernel evaluates it in float64 and
- * settles exact integer values of the argument with integer arithmetic.
+ * The ceiling is of the real number, decided exactly: the kernel's float64
+ * evaluation is used where it lies more than 1e-9 from an integer (its
+ * error is below 1e-10 in the supported domain); the few distances closer
+ * than that are decided on the host, before the launch, by an exact
+ * comparison of integer powers, and passed to the kernel.
  *
  * rel_idx : device int32[2*max_len - 1], written.
  * Errors  : INVALID_ARGUMENT for rel_idx == NULL, max_len < 1, or bucket
  *           parameters where the formula is undefined (position_buckets == 1,
  *           or max_relative_positions - 1 <= position_buckets/2 when
  *           bucketing, or max_relative_positions < 1 without);
- *           UNSUPPORTED for max_len > 65536; HIP_ERROR if the launch fails.
+ *           UNSUPPORTED for max_len > 65536, position_buckets > 4096, or
+ *           more than 32 near-integer distances (none is known to occur);
+ *           HIP_ERROR if the launch fails.
  */
 int rel_bucket(int32_t* rel_idx, int32_t max_len, int32_t position_buckets,
                int32_t max_relative_positions, hipStream_t stream);

@@ -119,7 +119,7 @@ def test_varlen_empty_is_noop(kw):
 @pytest.mark.parametrize("args,status", [
     ((None, 10, 256, 512), INV), ((A, 0, 256, 512), INV), ((A, 10, 1, 512), INV),
     ((A, 10, 256, 129), INV), ((A, 10, 0, 0), INV), ((A, 70000, 256, 512), UNS),
-    ((A + 2, 10, 256, 512), UNS),
+    ((A + 2, 10, 256, 512), UNS), ((A, 10, 4098, 9000), UNS),
 ])
 def test_rel_bucket_rejections(args, status):
     assert dd.lib().rel_bucket(*args, None) == status

@@ -41,6 +41,31 @@ def test_rel_bucket_bit_exact(max_len, P, M):
     assert np.array_equal(got.astype(np.int64), want)
 
 
+# bucket parameters: even and odd P, M just above P/2 to 2^31-1 (arguments that
+# come within 1e-10 of an integer without reaching it at P=16 and P=32 with
+# M = 2^31-1, exact integer arguments at P=32, M=129 and P=4, M=7)
+SWEEP = [(P, M) for P in (2, 3, 4, 5, 8, 9, 16, 17, 32, 64, 100, 256, 257, 512)
+         for M in sorted({P // 2 + 2, P, P + 1, 2 * P + 7, 129, 512, 1000, 65535, 2 ** 31 - 1})
+         if M - 1 > P // 2]
+
+
+LONG = [(16, 2 ** 31 - 1), (32, 2 ** 31 - 1), (32, 129), (4, 7), (256, 512), (512, 2 ** 31 - 1),
+        (1024, 4096), (4096, 70000)]
+
+
+def test_rel_bucket_sweep_bit_exact():
+    """Every (P, M) of SWEEP at max_len 600, and the LONG sets (which hold
+    the near-integer and exact-integer distances) at max_len 9000."""
+    n = 0
+    for max_len, sets in ((600, SWEEP), (9000, LONG)):
+        for P, M in sets:
+            got = H.gpu_table(max_len, P, M).cpu().numpy().astype(np.int64)
+            want = oracle.rel_index_table(max_len, P, M)
+            assert np.array_equal(got, want), (max_len, P, M, np.nonzero(got != want)[0][:5])
+            n += 1
+    _say(f"rel_bucket sweep: {n} (max_len, P, M) sets bit-exact")
+
+
 # ---------------------------------------------------------------------------
 # small shapes: every dtype, head dim, flag set and layout
 # ---------------------------------------------------------------------------
