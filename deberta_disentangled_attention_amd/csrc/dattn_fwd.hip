@@ -62,6 +62,7 @@ typedef float f32x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxSeqLen = 8192;
+constexpr int kShortPadded = 1024;   // padded lengths up to this order their items query tile first
 
 struct TBF16 {};
 struct TF16 {};
@@ -392,9 +393,10 @@ __device__ int block_first_true(int n, Pred pred, int* slot, int tid) {
 
 enum : int { TERM_OFF = 0, TERM_CONST = 1, TERM_BAND = 2 };
 
+// One work item: query tile qt of one (sequence, head). Every thread of the
+// workgroup calls it with the same item; it may return early (uniformly).
 template <class T, int D, int BN, int NW, bool VARLEN>
-__global__ __launch_bounds__(64 * NW, (Cfg<T, D, BN, NW>::WG_PER_CU))
-void dattn_fwd_kernel(FwdParams p) {
+__device__ __forceinline__ void fwd_item(const FwdParams& p, int item, unsigned char* smem) {
   typedef Cfg<T, D, BN, NW> C;
   constexpr int ES = C::ES;
   constexpr int BM = C::BM;
@@ -403,7 +405,6 @@ void dattn_fwd_kernel(FwdParams p) {
   constexpr int NC = C::NC;
   constexpr float NEG_INF = -__builtin_huge_valf();
 
-  __shared__ __attribute__((aligned(16))) unsigned char smem[C::LDS_BYTES];
   unsigned char* Ks = smem;
   unsigned char* Vt = smem + C::OFF_V;
   float* Ew = reinterpret_cast<float*>(smem + C::OFF_E);
@@ -420,16 +421,20 @@ void dattn_fwd_kernel(FwdParams p) {
   const int lh = lane >> 5;   // lane half: which 4-row groups / which k half
   float* Eww = Ew + wave * C::EW;
 
-  // ---- workgroup -> (sequence, head, query tile), XCD-aware ----------------
-  // Workgroups are handed to the 8 XCDs round-robin; renumber them so that
-  // each XCD receives a contiguous run of logical tiles (same head and
-  // sequence, hence the same K/V rows in that XCD's L2).
+  // ---- item -> (sequence, head, query tile), XCD-aware ----------------------
+  // Items are handed to the 8 XCDs round-robin; renumber them so that each
+  // XCD receives a contiguous run of logical tiles (same head and sequence,
+  // hence the same K/V rows in that XCD's L2). With qt_major (short padded
+  // batches with a mask) the query tile varies slowest instead, so the
+  // tiles that hold valid queries of right-padded rows are dispatched first
+  // and the zero-only ones last; K/V of short rows are small enough that no
+  // XCD grouping is needed.
   const int n_work = p.n_work;
-  const int hw = blockIdx.x;
+  const int hw = item;
   const int xcd = hw & 7;
   const int per = n_work >> 3;
   const int rem = n_work & 7;
-  const int logical = xcd * per + (xcd < rem ? xcd : rem) + (hw >> 3);
+  const int logical = p.qt_major ? hw : xcd * per + (xcd < rem ? xcd : rem) + (hw >> 3);
 
   int head, qt;
   int64_t base;        // token row of position 0 of the sequence
@@ -439,11 +444,20 @@ void dattn_fwd_kernel(FwdParams p) {
   const uint8_t* mrow = nullptr;
 
   if (!VARLEN) {
-    const int per_b = p.H * p.n_qtiles;
-    const int b = logical / per_b;
-    const int rest = logical - b * per_b;
-    head = rest / p.n_qtiles;
-    qt = rest - head * p.n_qtiles;
+    int b;
+    if (p.qt_major) {
+      const int per_qt = p.B * p.H;
+      qt = logical / per_qt;
+      const int rest = logical - qt * per_qt;
+      b = rest / p.H;
+      head = rest - b * p.H;
+    } else {
+      const int per_b = p.H * p.n_qtiles;
+      b = logical / per_b;
+      const int rest = logical - b * per_b;
+      head = rest / p.n_qtiles;
+      qt = rest - head * p.n_qtiles;
+    }
     base = (int64_t)b * p.L;
     row_limit = p.L;
     if (p.mask) {
@@ -1615,6 +1629,14 @@ void dattn_fwd_kernel(FwdParams p) {
   }
 }
 
+// one work item per workgroup
+template <class T, int D, int BN, int NW, bool VARLEN>
+__global__ __launch_bounds__(64 * NW, (Cfg<T, D, BN, NW>::WG_PER_CU))
+void dattn_fwd_kernel(FwdParams p) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[Cfg<T, D, BN, NW>::LDS_BYTES];
+  fwd_item<T, D, BN, NW, VARLEN>(p, blockIdx.x, smem);
+}
+
 // ----------------------------------------------------------------------------
 // host-side launch
 // ----------------------------------------------------------------------------
@@ -1633,6 +1655,11 @@ int launch_inst(FwdParams& p, bool varlen, hipStream_t stream) {
   if (n_work <= 0) return 0;
   if (n_work > 0x7fffffffLL) return 2;
   p.n_work = (int32_t)n_work;
+  // Short padded batches with a mask may hold many query tiles with no valid
+  // query (heavy right padding). Their items are ordered query tile first,
+  // so the workgroups dispatched first hold the valid tiles and the
+  // zero-only ones run behind them.
+  p.qt_major = (!varlen && p.mask && p.L <= kShortPadded) ? 1 : 0;
   if (varlen)
     hipLaunchKernelGGL((dattn_fwd_kernel<T, D, BN, NW, true>), dim3((unsigned)n_work), dim3(C::NT), 0,
                        stream, p);

@@ -34,7 +34,8 @@ struct FwdParams {
   float* lse;           // [tokens, H] natural log of each row's sum of exp(scores), or null
   int32_t max_seqlen;   // padded: L; packed: the caller's bound on every length
   int32_t n_qtiles;     // padded: query tiles per sequence; packed: tile slots
-  int32_t n_work;       // total workgroups launched
+  int32_t n_work;       // work items (query tiles of every (sequence, head)), one per workgroup
+  int32_t qt_major;     // padded only: items ordered query tile first
 };
 
 int launch_rel_bucket(int32_t* rel_idx, int32_t max_len, int32_t position_buckets,
