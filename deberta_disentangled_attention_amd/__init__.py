@@ -66,6 +66,18 @@ def lib() -> ctypes.CDLL:
         h.dattn_rel_proj.argtypes = [vp, i64, vp, vp, i64, vp, vp, vp, vp, i64, i32, i32, i32, i32,
                                      vp]
         h.dattn_rel_proj.restype = ctypes.c_int
+        h.rel_bucket_band.argtypes = [i32, i32, i32]
+        h.rel_bucket_band.restype = ctypes.c_int32
+        h.dattn_bwd_workspace_size.argtypes = [i64, i32, i32, i32, i32, i32]
+        h.dattn_bwd_workspace_size.restype = ctypes.c_int64
+        h.dattn_bwd_padded.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, i64, i64, vp, vp, vp, i64,
+                                       i32, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32,
+                                       i32, i32, i32, u32, f32, vp]
+        h.dattn_bwd_padded.restype = ctypes.c_int
+        h.dattn_bwd_varlen.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, i64, i64, vp, vp, vp, i64,
+                                       i32, vp, i32, i32, vp, i32, i32, i64, vp, vp, vp, vp, vp, vp,
+                                       i64, i32, i32, i32, u32, f32, vp]
+        h.dattn_bwd_varlen.restype = ctypes.c_int
         h.dattn_strerror.argtypes = [ctypes.c_int]
         h.dattn_strerror.restype = ctypes.c_char_p
         _lib_handle = h
@@ -238,6 +250,114 @@ def dattn_fwd_varlen(q, k, v, qr, kr, rel_idx, rel_max_len: int, cu_seqlens, max
         float(scale), _stream(q))
     _check(st, "dattn_fwd_varlen_lse")
     return out, lse
+
+
+def rel_bucket_band(max_len: int, position_buckets: int, max_relative_positions: int) -> int:
+    """The band of rel_bucket's table: the least W >= 1 beyond which (at
+    distances >= W and <= -W) the table is constant (host computation)."""
+    w = lib().rel_bucket_band(int(max_len), int(position_buckets), int(max_relative_positions))
+    if w < 1:
+        raise ValueError("invalid bucket parameters")
+    return int(w)
+
+
+def bwd_workspace_size(total_tokens: int, nseq: int, H: int, d: int, dtype, band: int) -> int:
+    import torch
+    code = {torch.float32: DATTN_F32, torch.float16: DATTN_F16, torch.bfloat16: DATTN_BF16}[dtype]
+    n = lib().dattn_bwd_workspace_size(int(total_tokens), int(nseq), int(H), int(d), code, int(band))
+    if n < 0:
+        raise ValueError("invalid workspace-size arguments")
+    return int(n)
+
+
+def _bwd_outputs(q, rows: int, H: int, d: int, n_rel: int, flags: int):
+    import torch
+    mk = lambda *shape: torch.empty(shape, dtype=q.dtype, device=q.device)
+    dq, dk, dv = mk(rows, H * d), mk(rows, H * d), mk(rows, H * d)
+    dqr = mk(n_rel, H * d) if flags else None
+    dkr = mk(n_rel, H * d) if flags else None
+    return dq, dk, dv, dqr, dkr
+
+
+def dattn_bwd_padded(q, k, v, out, dout, lse, qr, kr, rel_idx, rel_max_len: int, band: int, mask,
+                     H: int, d: int, *, flags: int = DATTN_C2P | DATTN_P2C, scale: float = 0.0,
+                     workspace=None):
+    """Backward of dattn_fwd_padded_lse: returns (dq, dk, dv, dqr, dkr); dq, dk,
+    dv are [B*L, H*d], dqr / dkr [n_rel, H*d] (None when flags == 0). out and
+    lse are the forward's; band bounds the distances where the table varies
+    (rel_bucket_band)."""
+    import torch
+    B, L = q.shape[0], q.shape[1]
+    for name, t in (("k", k), ("v", v), ("out", out), ("dout", dout)):
+        if t.shape[:2] != q.shape[:2] or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{name} must match q in [B, L], dtype and device")
+    lds = [_row_stride(t, n) for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout"))]
+    for t, ld, name in zip((q, k, v, out, dout), lds, ("q", "k", "v", "out", "dout")):
+        if B > 1 and t.stride(0) != L * ld:
+            raise ValueError(f"{name}: batch stride must be L * row stride")
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * L * H:
+        raise ValueError("lse must be the forward's contiguous float32 [B*L, H] log-sum-exp")
+    ld_rel, n_rel = 0, 0
+    if qr is not None:
+        if kr is None or kr.stride() != qr.stride() or kr.shape != qr.shape:
+            raise ValueError("qr and kr must have the same shape and strides")
+        ld_rel, n_rel = _row_stride(qr, "qr"), qr.shape[0]
+    _table_check(rel_idx, rel_max_len, flags, q.device)
+    if mask is not None:
+        if mask.dtype == torch.bool:
+            mask = mask.view(torch.uint8)
+        if mask.dtype != torch.uint8 or not mask.is_contiguous() or tuple(mask.shape) != (B, L):
+            raise ValueError("mask must be a contiguous [B, L] uint8/bool tensor")
+    band = int(band) if flags else 1
+    dq, dk, dv, dqr, dkr = _bwd_outputs(q, B * L, H, d, n_rel, flags)
+    need = bwd_workspace_size(B * L, B, H, d, q.dtype, band)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = lib().dattn_bwd_padded(
+        _ptr(q), _ptr(k), _ptr(v), lds[0], lds[1], lds[2], _ptr(out), _ptr(dout), lds[3], lds[4],
+        _ptr(lse), _ptr(qr), _ptr(kr), ld_rel, n_rel, _ptr(rel_idx), int(rel_max_len), band,
+        _ptr(mask), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dqr), _ptr(dkr), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), B, L, H, d, _dtype_code(q), int(flags),
+        float(scale), _stream(q))
+    _check(st, "dattn_bwd_padded")
+    return dq, dk, dv, dqr, dkr
+
+
+def dattn_bwd_varlen(q, k, v, out, dout, lse, qr, kr, rel_idx, rel_max_len: int, band: int,
+                     cu_seqlens, max_seqlen: int, H: int, d: int, *,
+                     flags: int = DATTN_C2P | DATTN_P2C, scale: float = 0.0, workspace=None):
+    """Backward of dattn_fwd_varlen_lse over packed sequences; returns (dq, dk,
+    dv, dqr, dkr) with dq, dk, dv [total_tokens, H*d]."""
+    import torch
+    T = q.shape[0]
+    for name, t in (("k", k), ("v", v), ("out", out), ("dout", dout)):
+        if t.shape[0] != T or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{name} must match q in rows, dtype and device")
+    lds = [_row_stride(t, n) for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout"))]
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != T * H:
+        raise ValueError("lse must be the forward's contiguous float32 [total_tokens, H] log-sum-exp")
+    if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous int32 tensor")
+    ld_rel, n_rel = 0, 0
+    if qr is not None:
+        if kr is None or kr.stride() != qr.stride() or kr.shape != qr.shape:
+            raise ValueError("qr and kr must have the same shape and strides")
+        ld_rel, n_rel = _row_stride(qr, "qr"), qr.shape[0]
+    _table_check(rel_idx, rel_max_len, flags, q.device)
+    nseq = cu_seqlens.numel() - 1
+    band = int(band) if flags else 1
+    dq, dk, dv, dqr, dkr = _bwd_outputs(q, T, H, d, n_rel, flags)
+    need = bwd_workspace_size(T, nseq, H, d, q.dtype, band)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = lib().dattn_bwd_varlen(
+        _ptr(q), _ptr(k), _ptr(v), lds[0], lds[1], lds[2], _ptr(out), _ptr(dout), lds[3], lds[4],
+        _ptr(lse), _ptr(qr), _ptr(kr), ld_rel, n_rel, _ptr(rel_idx), int(rel_max_len), band,
+        _ptr(cu_seqlens), nseq, int(max_seqlen), T, _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dqr),
+        _ptr(dkr), _ptr(workspace), workspace.numel() * workspace.element_size(), H, d,
+        _dtype_code(q), int(flags), float(scale), _stream(q))
+    _check(st, "dattn_bwd_varlen")
+    return dq, dk, dv, dqr, dkr
 
 
 def pack_index(mask, B: Optional[int] = None, L: Optional[int] = None, *, device=None):

@@ -164,6 +164,119 @@ int dattn_fwd_varlen_lse(const void* q, const void* k, const void* v, int64_t ld
                     lse, stream);
 }
 
+// ---------------------------------------------------------------------------
+// backward
+// ---------------------------------------------------------------------------
+
+int32_t rel_bucket_band(int32_t max_len, int32_t position_buckets, int32_t max_relative_positions) {
+  if (max_len < 1 || max_len > 65536) return -1;
+  if (position_buckets > 4096) return -1;
+  if (position_buckets > 0) {
+    const int mid = position_buckets / 2;
+    if (mid < 1 || max_relative_positions - 1 <= mid) return -1;
+  } else if (max_relative_positions < 1) {
+    return -1;
+  }
+  return dattn::rel_bucket_band_host(max_len, position_buckets, max_relative_positions);
+}
+
+int64_t dattn_bwd_workspace_size(int64_t total_tokens, int32_t nseq, int32_t H, int32_t d,
+                                 int32_t dtype, int32_t band) {
+  if (total_tokens < 0 || nseq < 0 || H < 1 || band < 1) return -1;
+  if (d != 32 && d != 64 && d != 128) return -1;
+  if (dtype != DATTN_F32 && dtype != DATTN_F16 && dtype != DATTN_BF16) return -1;
+  return dattn::bwd_workspace_bytes(total_tokens, nseq, H, d, esize_of(dtype), band);
+}
+
+static int bwd_common(const void* q, const void* k, const void* v, int64_t ld_q, int64_t ld_k,
+                      int64_t ld_v, const void* out, const void* dout, int64_t ld_o, int64_t ld_do,
+                      const float* lse, const void* qr, const void* kr, int64_t ld_rel,
+                      int32_t n_rel, const int32_t* rel_idx, int32_t rel_max_len, int32_t band,
+                      void* dq, void* dk, void* dv, void* dqr, void* dkr, void* workspace,
+                      int64_t workspace_bytes, int32_t H, int32_t d, int32_t dtype, uint32_t flags,
+                      float scale, int32_t seq_bound, dattn::BwdParams& p) {
+  int st = check_common(q, k, v, ld_q, ld_k, ld_v, qr, kr, ld_rel, n_rel, rel_idx, rel_max_len,
+                        dq, H, d, dtype, flags, scale, seq_bound);
+  if (st != DATTN_OK) return st;
+  if (!out || !dout || !lse || !dk || !dv || !workspace) return DATTN_ERR_INVALID_ARGUMENT;
+  const int64_t hd = (int64_t)H * d;
+  if (ld_o < hd || ld_do < hd) return DATTN_ERR_INVALID_ARGUMENT;
+  const int es = esize_of(dtype);
+  if (!aligned16(out) || !aligned16(dout) || !aligned16(dk) || !aligned16(dv) || !aligned4(lse) ||
+      !aligned16(workspace))
+    return DATTN_ERR_UNSUPPORTED;
+  if ((ld_o * es) % 16 || (ld_do * es) % 16) return DATTN_ERR_UNSUPPORTED;
+  if (flags) {
+    if (!dqr || !dkr) return DATTN_ERR_INVALID_ARGUMENT;
+    if (!aligned16(dqr) || !aligned16(dkr)) return DATTN_ERR_UNSUPPORTED;
+  }
+  // the distance store covers |u| < band; the table must be constant beyond
+  if (!flags) band = 1;   // ignored: no pair reads a table
+  if (band < 1 || band > (flags ? rel_max_len : 1)) return DATTN_ERR_INVALID_ARGUMENT;
+  p = dattn::BwdParams{};
+  p.q = q; p.k = k; p.v = v; p.o = out; p.dout = dout;
+  p.ld_q = ld_q; p.ld_k = ld_k; p.ld_v = ld_v; p.ld_o = ld_o; p.ld_do = ld_do;
+  p.lse = lse;
+  p.qr = qr; p.kr = kr; p.ld_rel = ld_rel; p.n_rel = n_rel;
+  p.rel_idx = rel_idx; p.rel_max_len = rel_max_len;
+  p.H = H; p.flags = flags;
+  const int terms = ((flags & DATTN_C2P) ? 1 : 0) + ((flags & DATTN_P2C) ? 1 : 0);
+  p.tau = scale > 0.f ? scale : (float)(1.0 / sqrt((double)d * (1 + terms)));
+  p.band = band;
+  p.dq = dq; p.dk = dk; p.dv = dv; p.dqr = dqr; p.dkr = dkr;
+  (void)workspace_bytes;
+  return DATTN_OK;
+}
+
+int dattn_bwd_padded(const void* q, const void* k, const void* v, int64_t ld_q, int64_t ld_k,
+                     int64_t ld_v, const void* out, const void* dout, int64_t ld_o, int64_t ld_do,
+                     const float* lse, const void* qr, const void* kr, int64_t ld_rel,
+                     int32_t n_rel, const int32_t* rel_idx, int32_t rel_max_len, int32_t band,
+                     const uint8_t* mask, void* dq, void* dk, void* dv, void* dqr, void* dkr,
+                     void* workspace, int64_t workspace_bytes, int32_t B, int32_t L, int32_t H,
+                     int32_t d, int32_t dtype, uint32_t flags, float scale, hipStream_t stream) {
+  if (B < 0 || L < 0) return DATTN_ERR_INVALID_ARGUMENT;
+  dattn::BwdParams p;
+  int st = bwd_common(q, k, v, ld_q, ld_k, ld_v, out, dout, ld_o, ld_do, lse, qr, kr, ld_rel, n_rel,
+                      rel_idx, rel_max_len, band, dq, dk, dv, dqr, dkr, workspace, workspace_bytes,
+                      H, d, dtype, flags, scale, L, p);
+  if (st != DATTN_OK) return st;
+  if ((int64_t)B * L == 0) return DATTN_OK;
+  const int64_t need = dattn::bwd_workspace_bytes((int64_t)B * L, B, H, d, esize_of(dtype), p.band);
+  if (workspace_bytes < need) return DATTN_ERR_INVALID_ARGUMENT;
+  p.mask = mask; p.B = B; p.L = L;
+  p.cu_seqlens = nullptr; p.nseq = 0;
+  p.tokens = (int64_t)B * L; p.units = B;
+  dattn::bwd_carve_workspace(p, workspace, d, esize_of(dtype));
+  return dattn::launch_bwd(p, dtype, d, false, stream);
+}
+
+int dattn_bwd_varlen(const void* q, const void* k, const void* v, int64_t ld_q, int64_t ld_k,
+                     int64_t ld_v, const void* out, const void* dout, int64_t ld_o, int64_t ld_do,
+                     const float* lse, const void* qr, const void* kr, int64_t ld_rel,
+                     int32_t n_rel, const int32_t* rel_idx, int32_t rel_max_len, int32_t band,
+                     const int32_t* cu_seqlens, int32_t nseq, int32_t max_seqlen,
+                     int64_t total_tokens, void* dq, void* dk, void* dv, void* dqr, void* dkr,
+                     void* workspace, int64_t workspace_bytes, int32_t H, int32_t d, int32_t dtype,
+                     uint32_t flags, float scale, hipStream_t stream) {
+  if (nseq < 0 || total_tokens < 0 || max_seqlen < 0) return DATTN_ERR_INVALID_ARGUMENT;
+  if (!cu_seqlens) return DATTN_ERR_INVALID_ARGUMENT;
+  if (!aligned4(cu_seqlens)) return DATTN_ERR_UNSUPPORTED;
+  dattn::BwdParams p;
+  int st = bwd_common(q, k, v, ld_q, ld_k, ld_v, out, dout, ld_o, ld_do, lse, qr, kr, ld_rel, n_rel,
+                      rel_idx, rel_max_len, band, dq, dk, dv, dqr, dkr, workspace, workspace_bytes,
+                      H, d, dtype, flags, scale, max_seqlen, p);
+  if (st != DATTN_OK) return st;
+  if (nseq == 0 || total_tokens == 0) return DATTN_OK;
+  const int64_t need = dattn::bwd_workspace_bytes(total_tokens, nseq, H, d, esize_of(dtype), p.band);
+  if (workspace_bytes < need) return DATTN_ERR_INVALID_ARGUMENT;
+  p.mask = nullptr; p.B = 0; p.L = 0;
+  p.cu_seqlens = cu_seqlens; p.nseq = nseq;
+  p.tokens = total_tokens; p.units = nseq;
+  dattn::bwd_carve_workspace(p, workspace, d, esize_of(dtype));
+  return dattn::launch_bwd(p, dtype, d, true, stream);
+}
+
 int dattn_pack_index(const uint8_t* mask, int32_t B, int32_t L, int32_t* cu_seqlens,
                      int32_t* token_rows, int32_t* row_to_packed, int32_t* max_seqlen,
                      hipStream_t stream) {

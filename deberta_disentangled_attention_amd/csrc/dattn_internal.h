@@ -38,8 +38,49 @@ struct FwdParams {
   int32_t qt_major;     // padded only: items ordered query tile first
 };
 
+// Arguments of the backward launches (device pointers; strides in elements).
+struct BwdParams {
+  const void* q; const void* k; const void* v; const void* o; const void* dout;
+  int64_t ld_q, ld_k, ld_v, ld_o, ld_do;
+  const float* lse;                 // [tokens, H]
+  const void* qr; const void* kr; int64_t ld_rel; int32_t n_rel;
+  const int32_t* rel_idx; int32_t rel_max_len;
+  const uint8_t* mask; int32_t B, L;         // padded layout
+  const int32_t* cu_seqlens; int32_t nseq;   // packed layout
+  int64_t tokens;                   // rows of every token array
+  int32_t units;                    // sequences
+  int32_t H;
+  uint32_t flags;
+  float tau;
+  int32_t band;                     // distances |u| < band are stored by distance
+  void* dq; void* dk; void* dv;     // [tokens, H*d]
+  void* dqr; void* dkr;             // [n_rel, H*d]
+  // workspace
+  float* dsum;                      // [tokens, H]
+  float* dq_part;                   // [tokens, H, d]
+  float* dk_part;                   // [tokens, H, d]
+  float* afar;                      // [tokens, H, 2]: query-side sums, u >= band / u <= -band
+  float* bfar;                      // [tokens, H, 2]: key-side sums, u >= band / u <= -band
+  void* dg;                         // [H, 2 band - 1, tokens] element type
+  float* wq;                        // [H, units, 2 band + 1, d]: distance sums with q, then the two far sums
+  float* wk;                        // [H, units, 2 band + 1, d]: with k
+  int32_t n_qtiles;                 // work items per (unit, head) or tile slots (packed)
+  int32_t n_work;
+};
+
+// bytes of the backward's workspace, and its layout
+int64_t bwd_workspace_bytes(int64_t tokens, int32_t units, int32_t H, int32_t d, int esize,
+                            int32_t band);
+void bwd_carve_workspace(BwdParams& p, void* ws, int d, int esize);
+// the backward's launches on `stream` (p without its workspace pointers carved)
+int launch_bwd(BwdParams& p, int dtype, int d, bool varlen, hipStream_t stream);
+
 int launch_rel_bucket(int32_t* rel_idx, int32_t max_len, int32_t position_buckets,
                       int32_t max_relative_positions, hipStream_t stream);
+// the table's band: the least W >= 1 such that every entry at distance
+// >= W equals the last entry and every entry at distance <= -W the first;
+// -1 when the parameters are invalid
+int32_t rel_bucket_band_host(int32_t max_len, int32_t P, int32_t M);
 
 // varlen = false: padded layout; true: packed layout.
 int launch_fwd(FwdParams& p, int dtype, int d, bool varlen, hipStream_t stream);

@@ -46,7 +46,7 @@ struct BucketFixes {
 
 // min(ceil(e ln(a/mid) / ln((M-1)/mid)), e + 2) for a > mid: with either
 // parity of P every offset from e + 2 on gives the table's first or last row
-__device__ int log_offset(int a, int mid, int M, const BucketFixes& fx) {
+__host__ __device__ int log_offset(int a, int mid, int M, const BucketFixes& fx) {
   const int e = mid - 1;
   if (e <= 0) return 0;
   if (a == M - 1) return e;   // the argument is exactly e there
@@ -61,12 +61,8 @@ __device__ int log_offset(int a, int mid, int M, const BucketFixes& fx) {
   return (int)ceil(x);
 }
 
-__global__ void rel_bucket_kernel(int32_t* __restrict__ out, int32_t max_len,
-                                  int32_t P, int32_t M, BucketFixes fx) {
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  const int n = 2 * max_len - 1;
-  if (idx >= n) return;
-  const int r = idx - (max_len - 1);
+// the table entry of distance r
+__host__ __device__ int table_entry(int r, int32_t P, int32_t M, const BucketFixes& fx) {
   int s, b;
   if (P <= 0) {
     s = M;
@@ -83,8 +79,15 @@ __global__ void rel_bucket_kernel(int32_t* __restrict__ out, int32_t max_len,
     }
   }
   int t = b + s;
-  t = t < 0 ? 0 : (t > 2 * s - 1 ? 2 * s - 1 : t);
-  out[idx] = t;
+  return t < 0 ? 0 : (t > 2 * s - 1 ? 2 * s - 1 : t);
+}
+
+__global__ void rel_bucket_kernel(int32_t* __restrict__ out, int32_t max_len,
+                                  int32_t P, int32_t M, BucketFixes fx) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  const int n = 2 * max_len - 1;
+  if (idx >= n) return;
+  out[idx] = table_entry(idx - (max_len - 1), P, M, fx);
 }
 
 // ---------------------------------------------------------------------------
@@ -159,6 +162,17 @@ bool find_fixes(int32_t max_len, int32_t P, int32_t M, BucketFixes& fx) {
 }
 
 }  // namespace
+
+int32_t rel_bucket_band_host(int32_t max_len, int32_t P, int32_t M) {
+  BucketFixes fx;
+  if (!find_fixes(max_len, P, M, fx)) return -1;
+  const int hi = table_entry(max_len - 1, P, M, fx), lo = table_entry(-(max_len - 1), P, M, fx);
+  // the table is non-decreasing: scan down from the longest distance to the
+  // first one whose entry (or its mirror's) differs from the end entries
+  for (int r = max_len - 1; r >= 1; --r)
+    if (table_entry(r, P, M, fx) != hi || table_entry(-r, P, M, fx) != lo) return r + 1;
+  return 1;
+}
 
 int launch_rel_bucket(int32_t* rel_idx, int32_t max_len, int32_t P, int32_t M,
                       hipStream_t stream) {

@@ -195,6 +195,96 @@ int dattn_fwd_varlen_lse(const void* q, const void* k, const void* v,
                          uint32_t flags, float scale, hipStream_t stream);
 
 /*
+ * Backward of the forward above: the gradients of a scalar loss with respect
+ * to q, k, v and the relative tables qr, kr, given dout = dLoss/dout. The
+ * pages' forward is inference-only (DisentangledFlash README "Status"); the
+ * kernels-community discussion #31 ("Packaging and validation") names the
+ * backward as the next step. With P the softmax weights (recomputed from the
+ * forward's log-sum-exp), D_i = dout_i . out_i and S the scaled scores:
+ *
+ *   dv_j   = sum_i P_ij dout_i
+ *   dS_ij  = P_ij (dout_i . v_j - D_i)            (0 for masked pairs)
+ *   dq_i   = scale sum_j dS_ij (k_j + [C2P] kr[T(i - j)])
+ *   dk_j   = scale sum_i dS_ij (q_i + [P2C] qr[T(j - i)])
+ *   dkr[r] = scale sum over pairs with T(i - j) = r of dS_ij q_i   [C2P]
+ *   dqr[r] = scale sum over pairs with T(j - i) = r of dS_ij k_j   [P2C]
+ *
+ * dkr and dqr collect every sequence of the batch (the tables are shared).
+ * The result is deterministic: every output element is produced by one
+ * thread from a reduction in a fixed order (no atomics), so repeated calls
+ * give identical bits.
+ *
+ * rel_bucket_band - the band of rel_bucket's table: the least W >= 1 such
+ * that every entry at a distance >= W equals the table's last entry and every
+ * entry at a distance <= -W its first (host computation, no device work);
+ * -1 for parameters rel_bucket rejects. For DeBERTa's 256/512 buckets it is
+ * 512 once max_len exceeds 512 (the last row is reached from distance 506
+ * on, the first only from -512 on).
+ */
+int32_t rel_bucket_band(int32_t max_len, int32_t position_buckets, int32_t max_relative_positions);
+
+/*
+ * dattn_bwd_workspace_size - bytes of device workspace the backward needs
+ * for total_tokens rows (B*L for the padded layout), nseq sequences (B for
+ * the padded layout), H heads of d, the element type and the band; -1 for
+ * invalid arguments. The workspace holds per-row statistics, fp32 partial
+ * dq/dk, and the dS of the pairs closer than `band` stored by distance
+ * (H * (2*band - 1) * total_tokens elements); with flags == 0 use band = 1.
+ */
+int64_t dattn_bwd_workspace_size(int64_t total_tokens, int32_t nseq, int32_t H, int32_t d,
+                                 int32_t dtype, int32_t band);
+
+/*
+ * dattn_bwd_padded, dattn_bwd_varlen - the backward.
+ *
+ * q, k, v, qr, kr, rel_idx, rel_max_len, mask / cu_seqlens, nseq,
+ *   max_seqlen, total_tokens, H, d, dtype, flags, scale: exactly as given to
+ *   the forward (dattn_fwd_padded_lse / dattn_fwd_varlen_lse).
+ * out, lse   : the forward's output and log-sum-exp of the same call;
+ *              out rows at stride ld_o.
+ * dout       : [rows, >=H*d] gradient of the output, stride ld_do.
+ * band       : W >= 1 such that rel_idx is constant beyond +-W (entries at
+ *              distances >= W equal its last entry, at <= -W its first), at
+ *              most rel_max_len; rel_bucket_band() gives it for rel_bucket's
+ *              tables, rel_max_len is always valid. Ignored when flags == 0.
+ * dq, dk, dv : [rows, H*d] contiguous, written completely (zero rows for
+ *              padded positions).
+ * dqr, dkr   : [n_rel, H*d] contiguous, written completely (rows no pair
+ *              reads are zero; a disabled term's table gradient is zero).
+ *              May be NULL when flags == 0.
+ * workspace  : device memory of at least dattn_bwd_workspace_size() bytes,
+ *              16-byte aligned, owned by the caller, overwritten; calls
+ *              that share a workspace must not overlap.
+ *
+ * Errors: those of the forward, plus INVALID_ARGUMENT for a NULL out, dout,
+ * lse, dk, dv, workspace (or dqr/dkr with flags != 0), ld_o / ld_do < H*d,
+ * band outside [1, rel_max_len] with flags != 0, or a workspace smaller
+ * than required; UNSUPPORTED for misaligned pointers or strides.
+ */
+int dattn_bwd_padded(const void* q, const void* k, const void* v,
+                     int64_t ld_q, int64_t ld_k, int64_t ld_v,
+                     const void* out, const void* dout, int64_t ld_o, int64_t ld_do,
+                     const float* lse,
+                     const void* qr, const void* kr, int64_t ld_rel, int32_t n_rel,
+                     const int32_t* rel_idx, int32_t rel_max_len, int32_t band,
+                     const uint8_t* mask, void* dq, void* dk, void* dv, void* dqr, void* dkr,
+                     void* workspace, int64_t workspace_bytes,
+                     int32_t B, int32_t L, int32_t H, int32_t d, int32_t dtype,
+                     uint32_t flags, float scale, hipStream_t stream);
+
+int dattn_bwd_varlen(const void* q, const void* k, const void* v,
+                     int64_t ld_q, int64_t ld_k, int64_t ld_v,
+                     const void* out, const void* dout, int64_t ld_o, int64_t ld_do,
+                     const float* lse,
+                     const void* qr, const void* kr, int64_t ld_rel, int32_t n_rel,
+                     const int32_t* rel_idx, int32_t rel_max_len, int32_t band,
+                     const int32_t* cu_seqlens, int32_t nseq, int32_t max_seqlen,
+                     int64_t total_tokens, void* dq, void* dk, void* dv, void* dqr, void* dkr,
+                     void* workspace, int64_t workspace_bytes,
+                     int32_t H, int32_t d, int32_t dtype,
+                     uint32_t flags, float scale, hipStream_t stream);
+
+/*
  * dattn_rel_proj - the per-head relative tables from the relative embeddings:
  *
  *   qr = E Wq^T + bq,   kr = E Wk^T + bk

@@ -263,3 +263,66 @@ def test_binding_rejects_bad_table_and_tokens_varlen():
                             out=torch.zeros(31, 64, dtype=torch.float16))
     with pytest.raises(ValueError, match="k must match"):
         dd.dattn_fwd_varlen(qp, qp.float(), qp, qr, qr, table, 16, cu, 16, 2, 32)
+
+
+# ---------------------------------------------------------------------------
+# backward entry points
+# ---------------------------------------------------------------------------
+
+def bwd_padded(**kw):
+    a = dict(q=A, k=A, v=A, ld_q=768, ld_k=768, ld_v=768, out=A, dout=A, ld_o=768, ld_do=768,
+             lse=A, qr=A, kr=A, ld_rel=768, n_rel=512, rel_idx=A, rel_max_len=512, band=512,
+             mask=None, dq=A, dk=A, dv=A, dqr=A, dkr=A, ws=A, ws_bytes=1 << 40, B=2, L=512, H=12,
+             d=64, dtype=dd.DATTN_BF16, flags=3, scale=0.0)
+    a.update(kw)
+    return dd.lib().dattn_bwd_padded(
+        a["q"], a["k"], a["v"], a["ld_q"], a["ld_k"], a["ld_v"], a["out"], a["dout"], a["ld_o"],
+        a["ld_do"], a["lse"], a["qr"], a["kr"], a["ld_rel"], a["n_rel"], a["rel_idx"],
+        a["rel_max_len"], a["band"], a["mask"], a["dq"], a["dk"], a["dv"], a["dqr"], a["dkr"],
+        a["ws"], a["ws_bytes"], a["B"], a["L"], a["H"], a["d"], a["dtype"], a["flags"], a["scale"],
+        None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dout=None), INV), (dict(lse=None), INV), (dict(ws=None), INV), (dict(dkr=None), INV),
+    (dict(band=0), INV), (dict(band=513), INV), (dict(ws_bytes=1000), INV), (dict(ld_do=100), INV),
+    (dict(d=48), UNS), (dict(dout=MIS), UNS), (dict(ws=A + 8), UNS), (dict(lse=A + 2), UNS),
+    (dict(B=-1), INV),
+])
+def test_bwd_rejections(kw, status):
+    assert bwd_padded(**kw) == status
+
+
+def test_bwd_empty_is_noop_and_flags0_needs_no_tables():
+    assert bwd_padded(B=0) == dd.DATTN_OK
+    assert bwd_padded(B=0, flags=0, qr=None, kr=None, rel_idx=None, dqr=None, dkr=None,
+                      band=0) == dd.DATTN_OK
+
+
+def test_bwd_workspace_size_and_band():
+    lib = dd.lib()
+    a = lib.dattn_bwd_workspace_size(131072, 16, 12, 64, dd.DATTN_BF16, 512)
+    b = lib.dattn_bwd_workspace_size(131072, 16, 12, 64, dd.DATTN_BF16, 1)
+    # the distance store grows by H * 2 * tokens elements per unit of band
+    assert a - b >= 12 * 2 * 511 * 131072 * 2
+    assert lib.dattn_bwd_workspace_size(10, 1, 1, 48, dd.DATTN_BF16, 1) == -1
+    assert lib.dattn_bwd_workspace_size(10, 1, 1, 64, dd.DATTN_BF16, 0) == -1
+    assert dd.rel_bucket_band(8192, 256, 512) == 512
+    assert dd.rel_bucket_band(128, 0, 64) == 64
+    assert lib.rel_bucket_band(10, 1, 512) == -1
+
+
+def test_rel_bucket_band_matches_the_oracle_table():
+    """The band is the least W with a constant table beyond +-W; checked on
+    the oracle's exact tables."""
+    import oracle
+    for args in [(8192, 256, 512), (512, 256, 512), (700, 16, 64), (300, 20, 64), (128, 0, 64),
+                 (1000, 0, 40), (3000, 4, 7)]:
+        T = oracle.rel_index_table(*args)
+        L = args[0]
+        w = 1
+        for r in range(L - 1, 0, -1):
+            if T[r + L - 1] != T[-1] or T[-r + L - 1] != T[0]:
+                w = r + 1
+                break
+        assert dd.rel_bucket_band(*args) == w, args
