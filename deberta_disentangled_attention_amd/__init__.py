@@ -21,6 +21,8 @@ DATTN_OK = 0
 DATTN_ERR_INVALID_ARGUMENT = 1
 DATTN_ERR_UNSUPPORTED = 2
 DATTN_ERR_HIP = 3
+DATTN_ERR_SCRATCH_TOO_SMALL = 4
+DATTN_NOALLOC_SCRATCH_BYTES = 128 << 20
 DATTN_F32, DATTN_F16, DATTN_BF16 = 0, 1, 2
 DATTN_C2P, DATTN_P2C = 1, 2
 DATTN_MAX_SEQLEN = 8192
@@ -78,6 +80,10 @@ def lib() -> ctypes.CDLL:
                                        i32, vp, i32, i32, vp, i32, i32, i64, vp, vp, vp, vp, vp, vp,
                                        i64, i32, i32, i32, u32, f32, vp]
         h.dattn_bwd_varlen.restype = ctypes.c_int
+        h.dattn_bwd_varlen_noalloc.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, i64, i64, vp, vp,
+                                               vp, i64, i32, vp, i32, i32, vp, i32, i32, i64, vp,
+                                               vp, vp, vp, vp, i32, i32, i32, u32, f32, vp]
+        h.dattn_bwd_varlen_noalloc.restype = ctypes.c_int
         h.dattn_strerror.argtypes = [ctypes.c_int]
         h.dattn_strerror.restype = ctypes.c_char_p
         _lib_handle = h
@@ -323,11 +329,8 @@ def dattn_bwd_padded(q, k, v, out, dout, lse, qr, kr, rel_idx, rel_max_len: int,
     return dq, dk, dv, dqr, dkr
 
 
-def dattn_bwd_varlen(q, k, v, out, dout, lse, qr, kr, rel_idx, rel_max_len: int, band: int,
-                     cu_seqlens, max_seqlen: int, H: int, d: int, *,
-                     flags: int = DATTN_C2P | DATTN_P2C, scale: float = 0.0, workspace=None):
-    """Backward of dattn_fwd_varlen_lse over packed sequences; returns (dq, dk,
-    dv, dqr, dkr) with dq, dk, dv [total_tokens, H*d]."""
+def _bwd_varlen_checks(q, k, v, out, dout, lse, qr, kr, rel_idx, rel_max_len, band, cu_seqlens,
+                       H, flags):
     import torch
     T = q.shape[0]
     for name, t in (("k", k), ("v", v), ("out", out), ("dout", dout)):
@@ -344,8 +347,18 @@ def dattn_bwd_varlen(q, k, v, out, dout, lse, qr, kr, rel_idx, rel_max_len: int,
             raise ValueError("qr and kr must have the same shape and strides")
         ld_rel, n_rel = _row_stride(qr, "qr"), qr.shape[0]
     _table_check(rel_idx, rel_max_len, flags, q.device)
-    nseq = cu_seqlens.numel() - 1
     band = int(band) if flags else 1
+    return T, lds, ld_rel, n_rel, cu_seqlens.numel() - 1, band
+
+
+def dattn_bwd_varlen(q, k, v, out, dout, lse, qr, kr, rel_idx, rel_max_len: int, band: int,
+                     cu_seqlens, max_seqlen: int, H: int, d: int, *,
+                     flags: int = DATTN_C2P | DATTN_P2C, scale: float = 0.0, workspace=None):
+    """Backward of dattn_fwd_varlen_lse over packed sequences; returns (dq, dk,
+    dv, dqr, dkr) with dq, dk, dv [total_tokens, H*d]."""
+    import torch
+    T, lds, ld_rel, n_rel, nseq, band = _bwd_varlen_checks(
+        q, k, v, out, dout, lse, qr, kr, rel_idx, rel_max_len, band, cu_seqlens, H, flags)
     dq, dk, dv, dqr, dkr = _bwd_outputs(q, T, H, d, n_rel, flags)
     need = bwd_workspace_size(T, nseq, H, d, q.dtype, band)
     if workspace is None:
@@ -357,6 +370,37 @@ def dattn_bwd_varlen(q, k, v, out, dout, lse, qr, kr, rel_idx, rel_max_len: int,
         _ptr(dkr), _ptr(workspace), workspace.numel() * workspace.element_size(), H, d,
         _dtype_code(q), int(flags), float(scale), _stream(q))
     _check(st, "dattn_bwd_varlen")
+    return dq, dk, dv, dqr, dkr
+
+
+def dattn_bwd_varlen_noalloc(q, k, v, out, dout, lse, qr, kr, rel_idx, rel_max_len: int,
+                             band: int, cu_seqlens, max_seqlen: int, H: int, d: int, *,
+                             flags: int = DATTN_C2P | DATTN_P2C, scale: float = 0.0, grads=None):
+    """dattn_bwd_varlen with the library's fixed per-GPU scratch array as its
+    workspace (no device allocation in the library call). grads, if given,
+    is the (dq, dk, dv, dqr, dkr) tuple to write (contiguous, q's dtype;
+    dqr/dkr may be None with flags == 0); otherwise the outputs are allocated
+    here. Calls that overlap on one GPU race."""
+    T, lds, ld_rel, n_rel, nseq, band = _bwd_varlen_checks(
+        q, k, v, out, dout, lse, qr, kr, rel_idx, rel_max_len, band, cu_seqlens, H, flags)
+    if grads is None:
+        grads = _bwd_outputs(q, T, H, d, n_rel, flags)
+    dq, dk, dv, dqr, dkr = grads
+    for name, t, rows in (("dq", dq, T), ("dk", dk, T), ("dv", dv, T), ("dqr", dqr, n_rel),
+                          ("dkr", dkr, n_rel)):
+        if t is None:
+            if flags or name in ("dq", "dk", "dv"):
+                raise ValueError(f"{name} is required")
+            continue
+        if (t.dtype != q.dtype or t.device != q.device or not t.is_contiguous()
+                or t.numel() != rows * H * d):
+            raise ValueError(f"{name} must be a contiguous [{rows}, {H * d}] tensor like q")
+    st = lib().dattn_bwd_varlen_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), lds[0], lds[1], lds[2], _ptr(out), _ptr(dout), lds[3], lds[4],
+        _ptr(lse), _ptr(qr), _ptr(kr), ld_rel, n_rel, _ptr(rel_idx), int(rel_max_len), band,
+        _ptr(cu_seqlens), nseq, int(max_seqlen), T, _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dqr),
+        _ptr(dkr), H, d, _dtype_code(q), int(flags), float(scale), _stream(q))
+    _check(st, "dattn_bwd_varlen_noalloc")
     return dq, dk, dv, dqr, dkr
 
 

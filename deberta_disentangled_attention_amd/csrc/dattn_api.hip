@@ -6,6 +6,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/dattn.h"
 #include "dattn_internal.h"
 
@@ -277,6 +279,71 @@ int dattn_bwd_varlen(const void* q, const void* k, const void* v, int64_t ld_q, 
   return dattn::launch_bwd(p, dtype, d, true, stream);
 }
 
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// allocation-free backward: the workspace lives in a fixed device array
+// ---------------------------------------------------------------------------
+
+// One copy per GPU, held from module load until the process ends. Host code
+// never passes `scratch` itself to a kernel (on the host the name is only a
+// stand-in): it uses the address hipGetSymbolAddress returns on each device.
+static __device__ __align__(256) unsigned char scratch[DATTN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // scratch's address on each device, once looked up
+
+// address of scratch on the current device (looked up on the first call there)
+int scratch_on_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DATTN_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return DATTN_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return DATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dattn_bwd_varlen_noalloc(const void* q, const void* k, const void* v, int64_t ld_q,
+                             int64_t ld_k, int64_t ld_v, const void* out, const void* dout,
+                             int64_t ld_o, int64_t ld_do, const float* lse, const void* qr,
+                             const void* kr, int64_t ld_rel, int32_t n_rel, const int32_t* rel_idx,
+                             int32_t rel_max_len, int32_t band, const int32_t* cu_seqlens,
+                             int32_t nseq, int32_t max_seqlen, int64_t total_tokens, void* dq,
+                             void* dk, void* dv, void* dqr, void* dkr, int32_t H, int32_t d,
+                             int32_t dtype, uint32_t flags, float scale, hipStream_t stream) {
+  if (nseq < 0 || total_tokens < 0 || max_seqlen < 0) return DATTN_ERR_INVALID_ARGUMENT;
+  if (!cu_seqlens) return DATTN_ERR_INVALID_ARGUMENT;
+  if (!aligned4(cu_seqlens)) return DATTN_ERR_UNSUPPORTED;
+  dattn::BwdParams p;
+  // the checks of dattn_bwd_varlen, with a stand-in workspace pointer
+  int st = bwd_common(q, k, v, ld_q, ld_k, ld_v, out, dout, ld_o, ld_do, lse, qr, kr, ld_rel, n_rel,
+                      rel_idx, rel_max_len, band, dq, dk, dv, dqr, dkr, reinterpret_cast<void*>(256),
+                      0, H, d, dtype, flags, scale, max_seqlen, p);
+  if (st != DATTN_OK) return st;
+  if (nseq == 0 || total_tokens == 0) return DATTN_OK;
+  const int64_t need = dattn::bwd_workspace_bytes(total_tokens, nseq, H, d, esize_of(dtype), p.band);
+  if (need > DATTN_NOALLOC_SCRATCH_BYTES) return DATTN_ERR_SCRATCH_TOO_SMALL;
+  void* ws = nullptr;
+  st = scratch_on_current_device(&ws);
+  if (st != DATTN_OK) return st;
+  p.mask = nullptr; p.B = 0; p.L = 0;
+  p.cu_seqlens = cu_seqlens; p.nseq = nseq;
+  p.tokens = total_tokens; p.units = nseq;
+  dattn::bwd_carve_workspace(p, ws, d, esize_of(dtype));
+  return dattn::launch_bwd(p, dtype, d, true, stream);
+}
+
 int dattn_pack_index(const uint8_t* mask, int32_t B, int32_t L, int32_t* cu_seqlens,
                      int32_t* token_rows, int32_t* row_to_packed, int32_t* max_seqlen,
                      hipStream_t stream) {
@@ -347,6 +414,9 @@ const char* dattn_strerror(int status) {
     case DATTN_ERR_INVALID_ARGUMENT: return "invalid argument";
     case DATTN_ERR_UNSUPPORTED: return "unsupported configuration";
     case DATTN_ERR_HIP: return "HIP launch failure";
+    case DATTN_ERR_SCRATCH_TOO_SMALL:
+      return "the problem needs more workspace than the allocation-free entry point's fixed "
+             "device array holds (DATTN_NOALLOC_SCRATCH_BYTES); use dattn_bwd_varlen with a workspace";
     default: return "unknown status";
   }
 }

@@ -55,6 +55,7 @@ extern "C" {
 #define DATTN_ERR_INVALID_ARGUMENT  1  /* null pointer, bad size, inconsistent lengths */
 #define DATTN_ERR_UNSUPPORTED       2  /* d, dtype, length > 8192, alignment or stride */
 #define DATTN_ERR_HIP               3  /* a HIP launch failed */
+#define DATTN_ERR_SCRATCH_TOO_SMALL 4  /* dattn_bwd_varlen_noalloc: problem exceeds its fixed array */
 
 /* element types */
 #define DATTN_F32   0
@@ -283,6 +284,41 @@ int dattn_bwd_varlen(const void* q, const void* k, const void* v,
                      void* workspace, int64_t workspace_bytes,
                      int32_t H, int32_t d, int32_t dtype,
                      uint32_t flags, float scale, hipStream_t stream);
+
+/*
+ * dattn_bwd_varlen_noalloc - dattn_bwd_varlen without a workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * The workspace is a fixed device array of DATTN_NOALLOC_SCRATCH_BYTES
+ * inside the library: one copy per GPU, held from the library's load until
+ * the process ends. The call allocates nothing (no hipMalloc, no allocating
+ * library routine); it uses the array of the current device, so the stream
+ * must belong to the current device. Every argument has the meaning it has
+ * in dattn_bwd_varlen, and the outputs are identical to its outputs.
+ *
+ * Every call on one GPU shares that GPU's array and leaves its contents
+ * behind (the call clears what must start at zero itself): two calls that
+ * overlap on one GPU, on different streams or host threads, race and give
+ * wrong results. Serialise them.
+ *
+ * Errors: those of dattn_bwd_varlen, plus DATTN_ERR_SCRATCH_TOO_SMALL when
+ * dattn_bwd_workspace_size() of the problem exceeds
+ * DATTN_NOALLOC_SCRATCH_BYTES (checked before any HIP call), and
+ * DATTN_ERR_HIP if the array's device address cannot be looked up.
+ */
+#define DATTN_NOALLOC_SCRATCH_BYTES (128ll << 20)
+
+int dattn_bwd_varlen_noalloc(const void* q, const void* k, const void* v,
+                             int64_t ld_q, int64_t ld_k, int64_t ld_v,
+                             const void* out, const void* dout, int64_t ld_o, int64_t ld_do,
+                             const float* lse,
+                             const void* qr, const void* kr, int64_t ld_rel, int32_t n_rel,
+                             const int32_t* rel_idx, int32_t rel_max_len, int32_t band,
+                             const int32_t* cu_seqlens, int32_t nseq, int32_t max_seqlen,
+                             int64_t total_tokens, void* dq, void* dk, void* dv, void* dqr,
+                             void* dkr, int32_t H, int32_t d, int32_t dtype,
+                             uint32_t flags, float scale, hipStream_t stream);
 
 /*
  * dattn_rel_proj - the per-head relative tables from the relative embeddings:

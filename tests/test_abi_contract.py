@@ -326,3 +326,13 @@ def test_rel_bucket_band_matches_the_oracle_table():
                 w = r + 1
                 break
         assert dd.rel_bucket_band(*args) == w, args
+
+
+def test_noalloc_rejects_problems_beyond_its_array_before_any_hip_call():
+    lib = dd.lib()
+    args = [A, A, A, 768, 768, 768, A, A, 768, 768, A, A, A, 768, 512, A, 8192, 512, A, 16, 8192,
+            131072, A, A, A, A, A, 12, 64, dd.DATTN_BF16, 3, 0.0, None]
+    assert lib.dattn_bwd_varlen_noalloc(*args) == dd.DATTN_ERR_SCRATCH_TOO_SMALL
+    assert b"allocation-free" in lib.dattn_strerror(dd.DATTN_ERR_SCRATCH_TOO_SMALL)
+    args[1] = None   # argument errors come first
+    assert lib.dattn_bwd_varlen_noalloc(*args) == INV
