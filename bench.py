@@ -354,6 +354,77 @@ def bench_relproj(args):
     }), flush=True)
 
 
+def bench_bwd(args):
+    """Time the backward (every launch of one dattn_bwd_* call) on the
+    workload, from the forward's output and log-sum-exp computed once.
+    Credited work is 2.5x the forward's effective flop: the five
+    L x L x d products of an attention backward (S and dP recomputed, dV,
+    dQ, dK) against the forward's two."""
+    import numpy as np
+    import torch
+    import deberta_disentangled_attention_amd as dd
+
+    w = build_workload(args.workload)
+    if args.flags is not None:
+        w.flags = args.flags
+    tdt = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(tdt).cuda()
+    q, k, v, qr, kr = dev(w.q), dev(w.k), dev(w.v), dev(w.qr), dev(w.kr)
+    relmax = w.max_seqlen if w.packed else w.L
+    table = dd.rel_bucket(relmax, w.position_buckets, w.max_relative_positions, device="cuda")
+    band = (dd.rel_bucket_band(relmax, w.position_buckets, w.max_relative_positions)
+            if w.flags else 1)
+    gen = torch.Generator(device="cpu").manual_seed(12345)
+    if w.packed:
+        cu = torch.from_numpy(w.cu_seqlens).cuda()
+        out, lse = dd.dattn_fwd_varlen(q, k, v, qr, kr, table, relmax, cu, w.max_seqlen, w.H,
+                                       w.d, flags=w.flags, lse=True)
+        dout = torch.randn(out.shape, generator=gen).to(tdt).cuda()
+        need = dd.bwd_workspace_size(w.total_tokens, w.B, w.H, w.d, tdt, band)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+
+        def bwd():
+            return dd.dattn_bwd_varlen(q, k, v, out, dout, lse, qr, kr, table, relmax, band, cu,
+                                       w.max_seqlen, w.H, w.d, flags=w.flags, workspace=ws)
+    else:
+        mask = None if w.mask is None else torch.from_numpy(w.mask).cuda()
+        out, lse = dd.dattn_fwd_padded(q, k, v, qr, kr, table, relmax, mask, w.H, w.d,
+                                       flags=w.flags, lse=True)
+        dout = torch.randn(out.shape, generator=gen).to(tdt).cuda()
+        need = dd.bwd_workspace_size(w.B * w.L, w.B, w.H, w.d, tdt, band)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+
+        def bwd():
+            return dd.dattn_bwd_padded(q, k, v, out, dout, lse, qr, kr, table, relmax, band, mask,
+                                       w.H, w.d, flags=w.flags, workspace=ws)
+
+    for _ in range(args.warmup):
+        bwd()
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    for a, b in events:
+        a.record()
+        bwd()
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in events)
+    avg = sum(ms) / len(ms)
+    flop = 2.5 * w.effective_flop()
+    peak = PEAK_TFLOPS[w.dtype]
+    print(json.dumps({
+        "metric": "disentangled attention backward (dq, dk, dv, dqr, dkr), effective TFLOP/s",
+        "workload": describe(w), "dtype": w.dtype, "flags": w.flags, "band": band,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_avg": round(avg, 4), "ms_median": round(ms[len(ms) // 2], 4),
+        "ms_min": round(ms[0], 4), "ms_max": round(ms[-1], 4),
+        "effective_flop": flop, "TFLOPs": round(flop / (avg * 1e-3) / 1e12, 2),
+        "pct_mfma_peak": round(100 * flop / (avg * 1e-3) / 1e12 / peak, 2),
+        "tokens_per_s": round(w.total_tokens / (avg * 1e-3), 1),
+        "workspace_bytes": int(need),
+    }), flush=True)
+
+
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--write-traffic":
         write_traffic(*sys.argv[2:6])
@@ -374,6 +445,8 @@ def main():
                     help="padded forward vs the device-packed route on a padded workload")
     ap.add_argument("--relproj", action="store_true",
                     help="time the qr/kr projection of the workload's table shape")
+    ap.add_argument("--bwd", action="store_true",
+                    help="time the backward on the workload (forward output and lse computed once)")
     ap.add_argument("--flush-l2", action="store_true",
                     help="overwrite a 512 MiB buffer before every step (outside the kernel's "
                          "events) so inputs are not served from L2 / Infinity Cache")
@@ -397,6 +470,9 @@ def main():
         if args.workload == "c4":
             args.workload = "c2"
         bench_relproj(args)
+        return
+    if args.bwd:
+        bench_bwd(args)
         return
     if args.pack:
         if args.workload == "c4":

@@ -67,17 +67,18 @@ struct BCfg {
   static constexpr int UPR = D * ES / 16;            // 16-byte units per row
   static constexpr int EPU = 16 / ES;
   static constexpr int RPITCH = D + EPU;             // staged row pitch (elements)
-  static constexpr int TPITCH = ES == 2 ? BY + 8 : BY + 4;   // transposed block pitch
   static constexpr int ROWS_BYTES = BY * RPITCH * ES;
-  static constexpr int TR_BYTES = (D * TPITCH * ES + 15) / 16 * 16;
+  static constexpr int NPF = (BY * UPR + NT - 1) / NT;   // 16-byte units per thread per staged block
+  // rows of the next block are loaded while the current one is computed,
+  // except where their registers do not fit (fp32, d = 128)
+  static constexpr bool PREFETCH = !(ES == 4 && D == 128);
   static constexpr int SCR_BYTES = 64 * 32 * 4;      // per wave: 64 distances x 32 positions
-  // LDS: two row blocks, two transposed blocks, per-wave scratch, per-y stats
+  // LDS: two row blocks, per-wave scratch, per-y stats
   static constexpr int OFF_R1 = 0;
   static constexpr int OFF_R2 = OFF_R1 + ROWS_BYTES;
-  static constexpr int OFF_T1 = OFF_R2 + ROWS_BYTES;
-  static constexpr int OFF_T2 = OFF_T1 + TR_BYTES;
-  static constexpr int OFF_SCR = OFF_T2 + TR_BYTES;
-  static constexpr int OFF_STAT = OFF_SCR + NW * SCR_BYTES;
+  static constexpr int OFF_SCR = OFF_R2 + ROWS_BYTES;
+  static constexpr int OFF_XF = OFF_SCR + NW * SCR_BYTES;   // per lane: the far-block operand
+  static constexpr int OFF_STAT = OFF_XF + NT * NU * 16;
   static constexpr int OFF_MISC = OFF_STAT + 2 * BY * 4;
   static constexpr int LDS_BYTES = OFF_MISC + 64;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -124,67 +125,74 @@ __device__ __forceinline__ int rel_row(const BwdParams& p, int dist) {
 
 template <class T>
 __global__ __launch_bounds__(256) void bwd_dsum_kernel(BwdParams p, int d) {
+  constexpr int EPU = 16 / Ty<T>::ESIZE;   // elements per 16-byte unit
   const int64_t stride = (int64_t)gridDim.x * 256;
   const int64_t rows = p.tokens * p.H;
+  const unsigned char* dob = reinterpret_cast<const unsigned char*>(p.dout);
+  const unsigned char* ob = reinterpret_cast<const unsigned char*>(p.o);
   for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < rows; idx += stride) {
     const int64_t t = idx / p.H;
     const int h = (int)(idx - t * p.H);
+    const unsigned char* a = dob + (t * p.ld_do + (int64_t)h * d) * Ty<T>::ESIZE;
+    const unsigned char* b = ob + (t * p.ld_o + (int64_t)h * d) * Ty<T>::ESIZE;
     float acc = 0.f;
-    for (int e = 0; e < d; ++e)
-      acc += to_f<T>(p.dout, t * p.ld_do + (int64_t)h * d + e) * to_f<T>(p.o, t * p.ld_o + (int64_t)h * d + e);
+    for (int e = 0; e < d; e += EPU) acc += dot16<T>(ld16(a + e * Ty<T>::ESIZE), ld16(b + e * Ty<T>::ESIZE));
     p.dsum[idx] = acc;
   }
-  // zero Dg: entries of pairs outside every sequence are never written
-  const int64_t n_dg = (int64_t)p.H * (2 * p.band - 1) * p.tokens;
-  for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < n_dg; x += stride) from_f<T>(p.dg, x, 0.f);
+  // zero the distance stores: entries of pairs outside every sequence are
+  // never written
+  if (p.flags) {
+    const int64_t units16 = (int64_t)p.H * p.dg_groups * p.dg_rows * 32 * Ty<T>::ESIZE / 16;
+    uint4* zq = reinterpret_cast<uint4*>(p.dgq);
+    uint4* zk = reinterpret_cast<uint4*>(p.dgk);
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < units16; x += stride) {
+      zq[x] = z;
+      zk[x] = z;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
 // 2./3. the tile loops
 // ---------------------------------------------------------------------------
 
-// Stage a block of BY rows (positions y0..y0+BY-1 of the unit, rows past
-// len are zero) into LDS: row-major (pitch RPITCH) and, optionally, the
-// transpose [D][BY] in the MFMA operand order of the forward's V^T.
+// A block of BY rows (positions y0 .. y0+BY-1 of the unit; rows of
+// positions past the extent or masked are zero) as 16-byte units, NPF per
+// thread: loaded into registers one block ahead, stored to LDS row-major
+// (pitch RPITCH) when the block's turn comes.
 template <class T, int D>
-__device__ __forceinline__ void stage_rows(const unsigned char* g, int64_t ld, int64_t tok0, int y0,
-                                           int ext, const uint8_t* mrow, int64_t hoff,
-                                           unsigned char* rows, unsigned char* tr, int tid) {
+__device__ __forceinline__ void load_rows(uint4* r, const unsigned char* g, int64_t ld,
+                                          int64_t tok0, int y0, int ext, const uint8_t* mrow, int64_t hoff,
+                                          int tid) {
   typedef BCfg<T, D> C;
-  constexpr int ES = C::ES;
-  constexpr int JOBS = (C::BY / 2) * C::UPR;   // (row pair, unit)
-  for (int x = tid; x < JOBS; x += C::NT) {
-    const int pr = x / C::UPR, u = x - pr * C::UPR;
-    uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
-    const int ya = y0 + 2 * pr, yb = ya + 1;
-    // rows of positions that take no part (past the extent, masked) are zero
-    if (ya < ext && (!mrow || mrow[ya])) a = ld16(g + ((tok0 + ya) * ld + hoff) * ES + 16 * u);
-    if (yb < ext && (!mrow || mrow[yb])) b = ld16(g + ((tok0 + yb) * ld + hoff) * ES + 16 * u);
-    *reinterpret_cast<uint4*>(rows + ((2 * pr) * C::RPITCH) * ES + 16 * u) = a;
-    *reinterpret_cast<uint4*>(rows + ((2 * pr + 1) * C::RPITCH) * ES + 16 * u) = b;
-    if (tr) {
-      const uint32_t a4[4] = {a.x, a.y, a.z, a.w}, b4[4] = {b.x, b.y, b.z, b.w};
-      if constexpr (ES == 2) {
-        uint32_t* t32 = reinterpret_cast<uint32_t*>(tr);
-        const int pp = v_pos(2 * pr) >> 1;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-          t32[(((8 * u + e) * C::TPITCH) >> 1) + pp] = __builtin_amdgcn_perm(b4[e >> 1], a4[e >> 1], sel);
-        }
-      } else {
-        uint2* t64 = reinterpret_cast<uint2*>(tr);
+  for (int k = 0; k < C::NPF; ++k) {
+    const int x = tid + k * C::NT;
+    const int row = x / C::UPR, u = x - row * C::UPR;
+    const int y = y0 + row;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (x < C::BY * C::UPR && y < ext && (!mrow || mrow[y])) v = ld16(g + ((tok0 + y) * ld + hoff) * C::ES + 16 * u);
+    r[k] = v;
+  }
+}
+
+template <class T, int D>
+__device__ __forceinline__ void store_rows(const uint4* r, unsigned char* rows, int tid) {
+  typedef BCfg<T, D> C;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) t64[((4 * u + e) * C::TPITCH + 2 * pr) >> 1] = make_uint2(a4[e], b4[e]);
-      }
-    }
+  for (int k = 0; k < C::NPF; ++k) {
+    const int x = tid + k * C::NT;
+    const int row = x / C::UPR, u = x - row * C::UPR;
+    if (x < C::BY * C::UPR) *reinterpret_cast<uint4*>(rows + row * C::RPITCH * C::ES + 16 * u) = r[k];
   }
 }
 
 // KSIDE = false: lanes own queries (x = i), the loop walks keys (y = j).
 // KSIDE = true:  lanes own keys (x = j), the loop walks queries (y = i).
 template <class T, int D, bool KSIDE, bool VARLEN>
-__global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
+// two workgroups per CU (two waves per SIMD) where the registers allow it
+__global__ __launch_bounds__(256, (D <= 64 && Ty<T>::ESIZE == 2) ? 2 : 1) void bwd_main_kernel(BwdParams p) {
   typedef BCfg<T, D> C;
   constexpr int ES = C::ES;
   constexpr int NU = C::NU;
@@ -194,8 +202,6 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[C::LDS_BYTES];
   unsigned char* R1 = smem + C::OFF_R1;   // rows for S: keys (Q side) / queries (K side)
   unsigned char* R2 = smem + C::OFF_R2;   // rows for dP: V (Q side) / dO (K side)
-  unsigned char* T1 = smem + C::OFF_T1;   // K^T (Q side) / dO^T (K side)
-  unsigned char* T2 = smem + C::OFF_T2;   // Q^T (K side)
   float* ystat = reinterpret_cast<float*>(smem + C::OFF_STAT);   // K side: lse, D of the block's queries
   int* misc = reinterpret_cast<int*>(smem + C::OFF_MISC);
 
@@ -245,7 +251,6 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
   const bool x_valid = x_in && (!mrow || mrow[x] != 0);
   const int64_t hoff = (int64_t)head * D;
   const float tau = p.tau;
-  const float l2e = 1.4426950408889634f;
   const bool c2p = (p.flags & 1u) != 0, p2c = (p.flags & 2u) != 0;
   // the "E" term reads the lane-side vector with table rows at T(x - y), the
   // "F" term the y-side rows with table rows at T(y - x)
@@ -296,12 +301,64 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
       xp[u] = x_valid ? ld16(gp + ((tok0 + x) * ldp + hoff + lh * C::HALF) * ES + 16 * u) : make_uint4(0, 0, 0, 0);
     }
   }
-  // Q side: this query's log-sum-exp and D
-  float lse_x = kNegInf, d_x = 0.f;
+  // P = exp2(S c1 - lse2) with c1 = tau log2(e) and lse2 = lse log2(e);
+  // lse2 = +inf for rows that take no part or have no valid key (P = 0)
+  const float l2e = 1.4426950408889634f;
+  const float c1 = p.tau * l2e;
+  const float kPosInf = __builtin_huge_valf();
+  float lse2_x = kPosInf, d_x = 0.f;   // Q side: this query's
   if (!KSIDE && x_valid) {
-    lse_x = p.lse[(tok0 + x) * p.H + head];
+    const float l = p.lse[(tok0 + x) * p.H + head];
+    lse2_x = l == kNegInf ? kPosInf : l * l2e;
     d_x = p.dsum[(tok0 + x) * p.H + head];
   }
+
+  // Blocks whose pairs all lie beyond the band (x - y >= band: "gt", or
+  // <= -band: "lt") read one table row per term: the E term is the lane
+  // scalar xs . ER[row] and the F term joins the S product through the
+  // operand xs + FR[row] (formed in fp32, rounded once to the element
+  // type). gt blocks come first in the loop, lt blocks last, so one operand
+  // set is live at a time.
+  const bool terms = e_on || f_on;
+  const int row_top = terms ? rel_row(p, p.rel_max_len - 1) : 0;
+  const int row_bot = terms ? rel_row(p, -(p.rel_max_len - 1)) : 0;
+  unsigned char* xf_lds = smem + C::OFF_XF + tid * NU * 16;   // this lane's far operand
+  float e_far = 0.f;
+  auto make_far = [&](bool lt) {
+    const int erow = lt ? row_bot : row_top, frow = lt ? row_top : row_bot;
+    if (f_on) {
+      uint4 rf[NU];
+      load_half_row<NU>(rf, FRg + (int64_t)frow * ld_rel_b);
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        if constexpr (ES == 2) {
+          const auto a = __builtin_bit_cast(typename Ty<T>::frag, xs[u]);
+          const auto b = __builtin_bit_cast(typename Ty<T>::frag, rf[u]);
+          f32x8_t sum;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sum[e] = (float)a[e] + (float)b[e];
+          *reinterpret_cast<uint4*>(xf_lds + 16 * u) = __builtin_bit_cast(uint4, Ty<T>::cvt8(sum));
+        } else {
+          const f32x4_t a = __builtin_bit_cast(f32x4_t, xs[u]), b = __builtin_bit_cast(f32x4_t, rf[u]);
+          *reinterpret_cast<uint4*>(xf_lds + 16 * u) = __builtin_bit_cast(uint4, a + b);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < NU; ++u) *reinterpret_cast<uint4*>(xf_lds + 16 * u) = xs[u];
+    }
+    float e = 0.f;
+    if (e_on) {
+      uint4 rf[NU];
+      load_half_row<NU>(rf, ERg + (int64_t)erow * ld_rel_b);
+#pragma unroll
+      for (int u = 0; u < NU; ++u) e += dot16<T>(xs[u], rf[u]);
+      e += __shfl_xor(e, 32);
+    }
+    e_far = e;
+  };
+  bool far_lt_ready = false;
+  if (terms) make_far(false);
 
   f32x16_t acc1[NDB], acc2[NDB];   // Q side: dQ^T; K side: dV^T (acc1), dK^T (acc2)
 #pragma unroll
@@ -309,15 +366,22 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
   float far_gt = 0.f, far_lt = 0.f;   // sums of dS over pairs with u >= band / u <= -band
   const int band = p.band;
 
-  constexpr int V_LANE = ES == 2 ? 8 : 4;
-  const unsigned char* t1_base = T1 + (li * C::TPITCH + V_LANE * lh) * ES;
-  const unsigned char* t2_base = T2 + (li * C::TPITCH + V_LANE * lh) * ES;
-  auto top = [](const unsigned char* base) {
+  // A operand of the gradient products: a staged block read transposed
+  // (m = the d index, the lane's; reduction over the block's positions y in
+  // the order the dS / P registers hold them: 16c + 4lh + {0-3, 8-11} for
+  // 16-bit types, 8c + 4lh + 0..3 for fp32)
+  auto top = [&](const unsigned char* rows) {
     return [=](int c, int db) {
-      if constexpr (ES == 2)
-        return __builtin_bit_cast(typename Ty<T>::frag, ld16(base + (db * 32 * C::TPITCH + 16 * c) * ES));
-      else
-        return *reinterpret_cast<const f32x4_t*>(base + (db * 32 * C::TPITCH + 8 * c) * ES);
+      if constexpr (ES == 2) {
+        const int g = lane >> 4, t = lane & 15;
+        const unsigned char* a =
+            rows + ((16 * c + 4 * (g >> 1) + (t >> 2)) * C::RPITCH + 32 * db + 16 * (g & 1) + 4 * (t & 3)) * 2;
+        const uint2 lo = lds_tr16(a), hi = lds_tr16(a + 8 * C::RPITCH * 2);
+        return __builtin_bit_cast(typename Ty<T>::frag, make_uint4(lo.x, lo.y, hi.x, hi.y));
+      } else {
+        const float* r = reinterpret_cast<const float*>(rows) + (8 * c + 4 * lh) * C::RPITCH + 32 * db + li;
+        return f32x4_t{r[0], r[C::RPITCH], r[2 * C::RPITCH], r[3 * C::RPITCH]};
+      }
     };
   };
   // acc[db] += (transposed block)^T-operand x frag
@@ -344,59 +408,154 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
     }
   };
 
-  const int64_t dg_rows = 2 * (int64_t)band - 1;
   const int y_end = ext;
-  for (int y0 = 0; y0 < y_end; y0 += C::BY) {
-    // ---- stage the block's rows ----------------------------------------------
+  // The next block's rows are loaded into registers while the current block
+  // is computed, with (K side) its queries' lse2 and D, (Q side) its keys'
+  // score bias (0, or -inf for keys that take no part) and whether every
+  // key of the block takes part.
+  uint4 pf1[C::NPF], pf2[C::NPF];
+  float pst0 = 0.f, pst1 = 0.f;
+  bool pfull = true;
+  auto fetch = [&](int yb) {
     if (!KSIDE) {
-      stage_rows<T, D>(Kg, p.ld_k, tok0, y0, ext, mrow, hoff, R1, T1, tid);
-      stage_rows<T, D>(Vg, p.ld_v, tok0, y0, ext, mrow, hoff, R2, nullptr, tid);
+      load_rows<T, D>(pf1, Kg, p.ld_k, tok0, yb, ext, mrow, hoff, tid);
+      load_rows<T, D>(pf2, Vg, p.ld_v, tok0, yb, ext, mrow, hoff, tid);
+      const int y = yb + li;
+      const bool ok = y < ext && (!mrow || mrow[y] != 0);
+      pst0 = ok ? 0.f : kNegInf;
+      pfull = __all(ok);
     } else {
-      stage_rows<T, D>(Qg, p.ld_q, tok0, y0, ext, mrow, hoff, R1, T2, tid);
-      stage_rows<T, D>(DOg, p.ld_do, tok0, y0, ext, mrow, hoff, R2, T1, tid);
+      load_rows<T, D>(pf1, Qg, p.ld_q, tok0, yb, ext, mrow, hoff, tid);
+      load_rows<T, D>(pf2, DOg, p.ld_do, tok0, yb, ext, mrow, hoff, tid);
       if (tid < C::BY) {
-        const int y = y0 + tid;
+        const int y = yb + tid;
         const bool ok = y < ext && (!mrow || mrow[y] != 0);
-        ystat[tid] = ok ? p.lse[(tok0 + y) * p.H + head] : kNegInf;
-        ystat[C::BY + tid] = ok ? p.dsum[(tok0 + y) * p.H + head] : 0.f;
+        const float l = ok ? p.lse[(tok0 + y) * p.H + head] : kNegInf;
+        pst0 = l == kNegInf ? kPosInf : l * l2e;
+        pst1 = ok ? p.dsum[(tok0 + y) * p.H + head] : 0.f;
       }
     }
-    __syncthreads();
+  };
+  // the block at y0 into LDS (ystat: K side lse2 and D of its queries, Q
+  // side its keys' bias), then the next block's loads go out; returns
+  // whether every y of the block takes part (Q side)
+  auto stage = [&](int y0) {
+    if (!C::PREFETCH) fetch(y0);
+    store_rows<T, D>(pf1, R1, tid);
+    store_rows<T, D>(pf2, R2, tid);
+    if (tid < C::BY) {
+      ystat[tid] = pst0;
+      ystat[C::BY + tid] = pst1;
+    }
+    const bool full = pfull;
+    lds_barrier();
+    if (C::PREFETCH && y0 + C::BY < y_end) fetch(y0 + C::BY);
+    return full;
+  };
 
-    // ---- scores of the block: lanes x, registers y ---------------------------
-    const unsigned char* r1_lane = R1 + (li * C::RPITCH + lh * C::HALF) * ES;
-    f32x16_t s = mma_chain_lds<T, NU, NC>(r1_lane, xs, f32x16_t{});
-    if (e_on) {
-      // E[u][x] = ER[T(umin + u)] . xs_x over the 63 distances u = x - y
-      const int umin = x0w - (y0 + 31);
-#pragma unroll
-      for (int ub = 0; ub < 2; ++ub) {
-        uint4 rf[NU];
-        load_half_row<NU>(rf, ERg + (int64_t)rel_row(p, umin + 32 * ub + li) * ld_rel_b);
-        const f32x16_t e = mma_chain<T, NU, NC>(rf, xs, f32x16_t{});
-#pragma unroll
-        for (int r = 0; r < 16; ++r) scr[(ub * 32 + rr_of(r) + 4 * lh) * 32 + li] = e[r];
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] += scr[(li - rr_of(r) - 4 * lh + 31) * 32 + li];
+  const unsigned char* r1_lane = R1 + (li * C::RPITCH + lh * C::HALF) * ES;
+  const unsigned char* r2_lane = R2 + (li * C::RPITCH + lh * C::HALF) * ES;
+  // the gradient products of a block from P (pm) and dS (ds)
+  auto grads = [&](const f32x16_t& pm, const f32x16_t& ds) {
+    if (!KSIDE) {
+      grad_acc(acc1, top(R1), ds);             // dQ^T += K^T dS
+    } else {
+      grad_acc(acc1, top(R2), pm);             // dV^T += dO^T P
+      grad_acc(acc2, top(R1), ds);             // dK^T += Q^T dS
     }
-    if (f_on) {
-      // F[y][v] = R1_y . FR[T(vmin + v)] over the 63 distances v = y - x
-      const int vmin = y0 - (x0w + 31);
+  };
+
+  // Blocks where every pair of the wave lies beyond the band on one side:
+  // one table row per term (E as the S accumulator's initial value, F in
+  // the operand), no per-pair tests. Returns the block's sum of dS.
+  auto far_block = [&](const uint4 (&xfr)[NU], bool full) {
+    f32x16_t s;
 #pragma unroll
-      for (int vb = 0; vb < 2; ++vb) {
-        uint4 rf[NU];
-        load_half_row<NU>(rf, FRg + (int64_t)rel_row(p, vmin + 32 * vb + li) * ld_rel_b);
-        const f32x16_t f = mma_chain_lds<T, NU, NC>(r1_lane, rf, f32x16_t{});
+    for (int r = 0; r < 16; ++r) s[r] = e_far;
+    s = mma_chain_lds<T, NU, NC>(r1_lane, xfr, s);
+    const f32x16_t dp = mma_chain_lds<T, NU, NC>(r2_lane, xp, f32x16_t{});
+    f32x16_t pm, ds;
+    float fs = 0.f;
+    if (!KSIDE) {
+      if (!full) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) scr[(rr_of(r) + 4 * lh) * 64 + vb * 32 + li] = f[r];
+        for (int r = 0; r < 16; ++r) s[r] += ystat[rr_of(r) + 4 * lh];
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] += scr[(rr_of(r) + 4 * lh) * 65 + 31 - li];
+      for (int r = 0; r < 16; ++r) {
+        const float pv = __builtin_amdgcn_exp2f(fmaf(s[r], c1, -lse2_x));
+        pm[r] = pv;
+        ds[r] = pv * (dp[r] - d_x);
+        fs += ds[r];
+      }
+    } else {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(ystat + 8 * g + 4 * lh);
+        const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(ystat + C::BY + 8 * g + 4 * lh);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          const float pv = __builtin_amdgcn_exp2f(fmaf(s[r], c1, -l4[e]));
+          pm[r] = pv;
+          ds[r] = pv * (dp[r] - d4[e]);
+          fs += ds[r];
+        }
+      }
+    }
+    grads(pm, ds);
+    return fs;
+  };
+
+  // Blocks with pairs inside the band (per wave: band products gathered
+  // along the diagonal, dS stored by distance), or beyond it on both sides.
+  auto general_block = [&](int y0) {
+    const int vlo = x0w - (y0 + 31), vhi = x0w + 31 - y0;   // x - y over the wave's block
+    const bool blk_far = terms && (vlo >= band || vhi <= -band);
+    f32x16_t s;
+    if (blk_far) {
+      if (vhi <= -band && !far_lt_ready) {
+        make_far(true);
+        far_lt_ready = true;
+      }
+      uint4 xf[NU];
+      lds_half_row<NU>(xf, xf_lds);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = e_far;
+      s = mma_chain_lds<T, NU, NC>(r1_lane, xf, s);
+    } else {
+      s = mma_chain_lds<T, NU, NC>(r1_lane, xs, f32x16_t{});
+      if (e_on) {
+        // E[u][x] = ER[T(umin + u)] . xs_x over the 63 distances u = x - y
+        const int umin = x0w - (y0 + 31);
+#pragma unroll
+        for (int ub = 0; ub < 2; ++ub) {
+          uint4 rf[NU];
+          load_half_row<NU>(rf, ERg + (int64_t)rel_row(p, umin + 32 * ub + li) * ld_rel_b);
+          const f32x16_t e = mma_chain<T, NU, NC>(rf, xs, f32x16_t{});
+#pragma unroll
+          for (int r = 0; r < 16; ++r) scr[(ub * 32 + rr_of(r) + 4 * lh) * 32 + li] = e[r];
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] += scr[(li - rr_of(r) - 4 * lh + 31) * 32 + li];
+      }
+      if (f_on) {
+        // F[y][v] = R1_y . FR[T(vmin + v)] over the 63 distances v = y - x
+        const int vmin = y0 - (x0w + 31);
+#pragma unroll
+        for (int vb = 0; vb < 2; ++vb) {
+          uint4 rf[NU];
+          load_half_row<NU>(rf, FRg + (int64_t)rel_row(p, vmin + 32 * vb + li) * ld_rel_b);
+          const f32x16_t f = mma_chain_lds<T, NU, NC>(r1_lane, rf, f32x16_t{});
+#pragma unroll
+          for (int r = 0; r < 16; ++r) scr[(rr_of(r) + 4 * lh) * 64 + vb * 32 + li] = f[r];
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] += scr[(rr_of(r) + 4 * lh) * 65 + 31 - li];
+      }
     }
 
-    // ---- P, dP, dS -------------------------------------------------------------
-    const unsigned char* r2_lane = R2 + (li * C::RPITCH + lh * C::HALF) * ES;
+    // P, dP, dS with every pair tested
     const f32x16_t dp = mma_chain_lds<T, NU, NC>(r2_lane, xp, f32x16_t{});
     f32x16_t pm, ds;
 #pragma unroll
@@ -404,24 +563,16 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
       const int yr = rr_of(r) + 4 * lh;
       const int y = y0 + yr;
       const bool y_valid = y < ext && (!mrow || mrow[y] != 0);
-      float lse_i, d_i;
-      if (!KSIDE) { lse_i = lse_x; d_i = d_x; }
-      else { lse_i = ystat[yr]; d_i = ystat[C::BY + yr]; }
-      const bool ok = x_valid && y_valid && lse_i != kNegInf;
-      const float pv = ok ? __builtin_amdgcn_exp2f((s[r] * tau - lse_i) * l2e) : 0.f;
+      const float lse_i = KSIDE ? ystat[yr] : lse2_x;
+      const float d_i = KSIDE ? ystat[C::BY + yr] : d_x;
+      const bool ok = x_valid && y_valid;
+      const float pv = ok ? __builtin_amdgcn_exp2f(fmaf(s[r], c1, -lse_i)) : 0.f;
       pm[r] = pv;
       ds[r] = ok ? pv * (dp[r] - d_i) : 0.f;
     }
+    grads(pm, ds);
 
-    // ---- gradient products -----------------------------------------------------
-    if (!KSIDE) {
-      grad_acc(acc1, top(t1_base), ds);        // dQ^T += K^T dS
-    } else {
-      grad_acc(acc1, top(t1_base), pm);        // dV^T += dO^T P
-      grad_acc(acc2, top(t2_base), ds);        // dK^T += Q^T dS
-    }
-
-    // ---- pairs beyond the band: per-position sums; inside (Q side): Dg --------
+    // pairs beyond the band: per-position sums; inside: the distance store
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int y = y0 + rr_of(r) + 4 * lh;
@@ -429,30 +580,95 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
       if (u >= band) far_gt += ds[r];
       else if (u <= -band) far_lt += ds[r];
     }
-    if (!KSIDE) {
-      // dS of this wave's pairs by distance u = x - y: scratch [u - umin][x]
-      const int umin = x0w - (y0 + 31);
+    if (e_on && !blk_far) {
+      // dS of this wave's pairs by query-minus-key distance u into scratch
+      // [u - umin][x], then into the store indexed by the lane's token: rows
+      // u hold consecutive tokens (lanes 0-31 write row 2k, 32-63 row 2k+1)
+      const int umin = KSIDE ? y0 - (x0w + 31) : x0w - (y0 + 31);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) scr[(li - rr_of(r) - 4 * lh + 31) * 32 + li] = ds[r];
-      // rows u of Dg hold consecutive query tokens: lanes 0-31 write row
-      // 2k, lanes 32-63 row 2k+1
-      for (int k2 = 0; k2 < 32; ++k2) {
+      for (int r = 0; r < 16; ++r) {
+        const int yr = rr_of(r) + 4 * lh;
+        scr[(KSIDE ? yr - li + 31 : li - yr + 31) * 32 + li] = ds[r];
+      }
+      // row ui holds the pair (x, y) of this block iff ui - li (Q side) or
+      // ui + li - 31 (K side) is in [0, 31]; rows past the band, positions
+      // past the extent and lanes outside the unit write nothing
+      using E = typename std::conditional<ES == 2, uint16_t, float>::type;
+      const int64_t t = tok0 + x;
+      E* ptr = reinterpret_cast<E*>(KSIDE ? p.dgk : p.dgq) +
+               (((int64_t)head * p.dg_groups + (t >> 5)) * p.dg_rows + (umin + lh + p.dg_rb)) * 32 + (t & 31);
+      const int64_t step = 64;   // two rows
+      const bool inner = umin > -band && umin + 62 < band && y0 + C::BY <= ext;   // wave-uniform
+#pragma unroll 4
+      for (int k2 = 0; k2 < 32; ++k2, ptr += step) {
         const int ui = 2 * k2 + lh;
-        const int u = umin + ui;
-        const int y = x - u;
-        if (ui < 63 && u > -band && u < band && x_in && y >= y0 && y < y0 + C::BY && y < ext) {
-          const int64_t idx = ((int64_t)head * dg_rows + (u + band - 1)) * p.tokens + tok0 + x;
-          from_f<T>(p.dg, idx, scr[ui * 32 + li]);
+        const int yo = KSIDE ? ui + li - 31 : li + 31 - ui;   // y - y0 of the pair in row ui
+        bool ok = x_in && (unsigned)yo < 32u;
+        if (!inner) {
+          const int u = umin + ui;
+          ok = ok && u > -band && u < band && y0 + yo < ext;
+        }
+        if (ok) {
+          const float v = scr[ui * 32 + li];
+          if constexpr (ES == 2) *ptr = __builtin_bit_cast(uint16_t, (typename std::conditional<std::is_same<T, TF16>::value, _Float16, __bf16>::type)v);
+          else *ptr = v;
         }
       }
     }
-    __syncthreads();   // the block's LDS is rewritten next
+  };
+
+  // Block ranges: [0, n_gt) beyond the band below for every wave (u >= band
+  // on the Q side), [n_lt, nb) beyond it above for every wave, the rest
+  // general. Without position terms every block takes the plain path.
+  const int nb = (y_end + C::BY - 1) / C::BY;
+  int n_gt = nb, n_lt = nb;
+  if (terms) {
+    const int lim = x0 - 31 - band;                 // y0 <= lim: wave 0 (the closest) beyond the band
+    n_gt = lim >= 0 ? min(nb, lim / C::BY + 1) : 0;
+    const int lo = x0 + (C::BX - 1) + band;         // y0 >= lo: the last wave beyond the band
+    n_lt = max(n_gt, min(nb, (lo + C::BY - 1) / C::BY));
+  }
+  if (C::PREFETCH) fetch(0);
+  if (n_gt > 0) {
+    uint4 xf[NU];
+    if (terms) lds_half_row<NU>(xf, xf_lds);
+    else {
+#pragma unroll
+      for (int u = 0; u < NU; ++u) xf[u] = xs[u];
+    }
+    float fs = 0.f;
+    for (int n = 0; n < n_gt; ++n) {
+      const bool full = stage(n * C::BY);
+      fs += far_block(xf, full);
+      lds_barrier();   // the block's LDS is rewritten next
+    }
+    // KSIDE: these blocks have y - x <= -band, i.e. query minus key <= -band
+    if (KSIDE) far_lt += fs;
+    else far_gt += fs;
+  }
+  for (int n = n_gt; n < n_lt; ++n) {
+    stage(n * C::BY);
+    general_block(n * C::BY);
+    lds_barrier();   // the block's LDS is rewritten next; its stores may still be in flight
+  }
+  if (n_lt < nb) {
+    if (!far_lt_ready) make_far(true);
+    uint4 xf[NU];
+    lds_half_row<NU>(xf, xf_lds);
+    float fs = 0.f;
+    for (int n = n_lt; n < nb; ++n) {
+      const bool full = stage(n * C::BY);
+      fs += far_block(xf, full);
+      lds_barrier();
+    }
+    if (KSIDE) far_gt += fs;
+    else far_lt += fs;
   }
 
   // ---- epilogue --------------------------------------------------------------
   const float fgt = far_gt + __shfl_xor(far_gt, 32);   // both lane halves of position x
   const float flt = far_lt + __shfl_xor(far_lt, 32);
-  if (!x_in) {
+  if (!x_valid) {   // past the extent or masked: zero gradients
     write_zero_row();
     return;
   }
@@ -477,160 +693,275 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// 4. position parts of dQ (C2P) and dK (P2C); every row rounded once
+// 4.-5. the distance sums as MFMA products
 // ---------------------------------------------------------------------------
 
-// KSIDE = false: dq[t] = dq_part[t] + tau (sum_u Dg[u][t] kr[T(u)]
-//                          + afar_gt[t] kr[top] + afar_lt[t] kr[bottom])
-// KSIDE = true:  dk[t] = dk_part[t] + tau (sum_u Dg[u][t+u] qr[T(-u)]
-//                          + bfar_gt[t] qr[bottom] + bfar_lt[t] qr[top])
-// (beyond the band C2P reads the top row for u >= band and the bottom row
-// for u <= -band; P2C, which reads T(-u), the other way round.)
-// One workgroup per (32 tokens, head); distances in chunks of 64 through LDS.
-template <class T, bool KSIDE>
-__global__ __launch_bounds__(256) void bwd_pos_grad_kernel(BwdParams p, int d) {
-  constexpr int TB = 32, UB = 64;
-  const int head = blockIdx.y;
-  const int64_t t0 = (int64_t)blockIdx.x * TB;
-  const bool on = KSIDE ? (p.flags & 2u) != 0 : (p.flags & 1u) != 0;
-  const void* rel = KSIDE ? p.qr : p.kr;
-  const float* part = KSIDE ? p.dk_part : p.dq_part;
-  const float* fars = KSIDE ? p.bfar : p.afar;
-  void* outp = KSIDE ? p.dk : p.dq;
-  const int band = p.band;
-  const int64_t dg_rows = 2 * (int64_t)band - 1;
-  __shared__ float dgs[UB][TB + 1];
-  __shared__ float rrow[UB][128 + 1];
-  // this thread's outputs: column c, tokens tg, tg + per, ...
-  const int c = threadIdx.x % d;
-  const int per = 256 / d;                 // token groups
-  const int tg = threadIdx.x / d;
-  constexpr int MAXK = TB / 2;             // d >= 32: at most 16 tokens per thread
-  const int nk = TB / per;
-  float acc[MAXK];
-#pragma unroll
-  for (int k = 0; k < MAXK; ++k) acc[k] = 0.f;
-  if (on) {
-    for (int u0 = -(band - 1); u0 < band; u0 += UB) {
-      __syncthreads();
-      for (int x = threadIdx.x; x < UB * TB; x += 256) {
-        const int ui = x / TB, tt = x - ui * TB;
-        const int u = u0 + ui;
-        float val = 0.f;
-        const int64_t col = t0 + tt + (KSIDE ? u : 0);
-        if (u < band && t0 + tt < p.tokens && col >= 0 && col < p.tokens)
-          val = to_f<T>(p.dg, ((int64_t)head * dg_rows + (u + band - 1)) * p.tokens + col);
-        dgs[ui][tt] = val;
-      }
-      for (int x = threadIdx.x; x < UB * d; x += 256) {
-        const int ui = x / d, e = x - ui * d;
-        const int u = u0 + ui;
-        rrow[ui][e] = u < band ? to_f<T>(rel, (int64_t)rel_row(p, KSIDE ? -u : u) * p.ld_rel + (int64_t)head * d + e)
-                               : 0.f;
-      }
-      __syncthreads();
-      const int nu = min(UB, band - u0);
-      for (int ui = 0; ui < nu; ++ui) {
-        const float rv = rrow[ui][c];
-#pragma unroll
-        for (int k = 0; k < MAXK; ++k)
-          if (k < nk) acc[k] += dgs[ui][tg + k * per] * rv;
-      }
-    }
-  }
-  const int row_top = on ? rel_row(p, p.rel_max_len - 1) : 0;
-  const int row_bot = on ? rel_row(p, -(p.rel_max_len - 1)) : 0;
-  const int r_gt = KSIDE ? row_bot : row_top, r_lt = KSIDE ? row_top : row_bot;
-#pragma unroll
-  for (int k = 0; k < MAXK; ++k) {
-    const int64_t t = t0 + tg + k * per;
-    if (k >= nk || t >= p.tokens) continue;
-    float a = acc[k];
-    if (on) {
-      a += fars[(t * p.H + head) * 2 + 0] * to_f<T>(rel, (int64_t)r_gt * p.ld_rel + (int64_t)head * d + c);
-      a += fars[(t * p.H + head) * 2 + 1] * to_f<T>(rel, (int64_t)r_lt * p.ld_rel + (int64_t)head * d + c);
-    }
-    from_f<T>(outp, t * ((int64_t)p.H * d) + (int64_t)head * d + c,
-              part[(t * p.H + head) * d + c] + p.tau * a);
+// MFMA operand of lane (n = lane % 32, reduction elements k0 + 8 (lane / 32)
+// + 0..7 for 16-bit types, k0 + lane / 32 for fp32) from a row-major LDS
+// block [k][n] with `pitch` elements per row: the transposing read
+// ds_read_b64_tr_b16 for 16-bit types (two reads of four rows each).
+template <class T>
+__device__ __forceinline__ typename Ty<T>::frag kop_rows(const unsigned char* blk, int pitch, int k0,
+                                                       int n0, int lane) {
+  if constexpr (Ty<T>::ESIZE == 2) {
+    const int g = lane >> 4, t = lane & 15;
+    const unsigned char* a =
+        blk + ((k0 + 8 * (g >> 1) + (t >> 2)) * pitch + n0 + 16 * (g & 1) + 4 * (t & 3)) * 2;
+    const uint2 lo = lds_tr16(a), hi = lds_tr16(a + 4 * pitch * 2);
+    return __builtin_bit_cast(typename Ty<T>::frag, make_uint4(lo.x, lo.y, hi.x, hi.y));
+  } else {
+    return reinterpret_cast<const float*>(blk)[(k0 + (lane >> 5)) * pitch + n0 + (lane & 31)];
   }
 }
 
-// ---------------------------------------------------------------------------
-// 5. per (head, unit): W_u = sum_i Dg[u][i] q_i (C2P) and sum_j Dg[u][j+u] k_j
-//    (P2C) for |u| < band; then the beyond-band sums times q and k
-// ---------------------------------------------------------------------------
-
-// Rows of W: 0 .. 2band-2 are the distances u = row - (band-1); row 2band-1
-// holds the u >= band sums, row 2band the u <= -band sums. One workgroup per
-// (64 rows, unit, head); positions in chunks of 32 through LDS.
+// MFMA operand of lane (m = lane % 32, the same reduction elements) from a
+// row-major LDS block [m][k] (reduction index contiguous)
 template <class T>
-__global__ __launch_bounds__(256) void bwd_pos_w_kernel(BwdParams p, int d) {
-  constexpr int RB = 64, IB = 32;
+__device__ __forceinline__ typename Ty<T>::frag mop_rows(const unsigned char* blk, int pitch, int k0,
+                                                       int m0, int lane) {
+  if constexpr (Ty<T>::ESIZE == 2) {
+    return __builtin_bit_cast(typename Ty<T>::frag,
+                              ld16(blk + ((m0 + (lane & 31)) * pitch + k0 + 8 * (lane >> 5)) * 2));
+  } else {
+    return reinterpret_cast<const float*>(blk)[(m0 + (lane & 31)) * pitch + k0 + (lane >> 5)];
+  }
+}
+
+// Position parts of dQ (C2P, KSIDE = false) and dK (P2C, KSIDE = true):
+//   dq[t] = dq_part[t] + tau (sum_u Dq[u][t] kr[T(u)]
+//                             + afar_gt[t] kr[top] + afar_lt[t] kr[bottom])
+//   dk[t] = dk_part[t] + tau (sum_u Dk[u][t] qr[T(-u)]
+//                             + bfar_gt[t] qr[bottom] + bfar_lt[t] qr[top])
+// (u is query minus key; beyond the band C2P reads the top row for u >= band
+// and the bottom row for u <= -band, P2C the other way round). As a product
+// out^T [d x tokens] = R^T [d x U] D [U x tokens]: a workgroup owns 128
+// tokens of one head (32 per wave) and walks the distances 32 at a time;
+// the D block and the gathered table rows are staged row-major in LDS and
+// both operands are read transposed. Every output row is rounded once.
+template <class T, int D, bool KSIDE>
+__global__ __launch_bounds__(256) void bwd_pos_grad_kernel(BwdParams p) {
+  constexpr int ES = Ty<T>::ESIZE;
+  constexpr int TB = 128, UB = 32, EPU = 16 / ES;
+  constexpr int DP = TB + 32 / ES;     // D block pitch (elements): rows 32 bytes apart in the banks
+  constexpr int RP = D + 32 / ES;      // table block pitch
+  constexpr int NDB = D / 32;
+  constexpr int KSTEP = ES == 2 ? 16 : 2;
+  __shared__ __attribute__((aligned(16))) unsigned char dsb[UB * DP * ES];
+  __shared__ __attribute__((aligned(16))) unsigned char rsb[UB * RP * ES];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 31, lh = lane >> 5;
+  const int head = blockIdx.y;
+  const int64_t t0 = (int64_t)blockIdx.x * TB;
+  const bool on = KSIDE ? (p.flags & 2u) != 0 : (p.flags & 1u) != 0;
+  const unsigned char* rel = reinterpret_cast<const unsigned char*>(KSIDE ? p.qr : p.kr);
+  const unsigned char* dgs = reinterpret_cast<const unsigned char*>(KSIDE ? p.dgk : p.dgq);
+  const int band = p.band;
+
+  f32x16_t acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x16_t{};
+  if (on) {
+    for (int u0 = -(band - 1); u0 < band; u0 += UB) {
+      // D rows u0 .. u0+31 over tokens t0 .. t0+127: four 32-token groups
+      // (groups past the last token and rows past the band read as zero)
+      for (int x = tid; x < UB * (TB / EPU); x += 256) {
+        const int r = x / (TB / EPU), c = x - r * (TB / EPU);
+        const int u = u0 + r;
+        const int64_t g = (t0 >> 5) + c / (32 / EPU);
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (u < band && g < p.dg_groups)
+          v = ld16(dgs + ((((int64_t)head * p.dg_groups + g) * p.dg_rows + (u + p.dg_rb)) * 32 +
+                          EPU * (c % (32 / EPU))) * ES);
+        *reinterpret_cast<uint4*>(dsb + (r * DP + EPU * c) * ES) = v;
+      }
+      // the table rows these distances read
+      for (int x = tid; x < UB * (D / EPU); x += 256) {
+        const int r = x / (D / EPU), c = x - r * (D / EPU);
+        const int u = u0 + r;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (u < band) v = ld16(rel + ((int64_t)rel_row(p, KSIDE ? -u : u) * p.ld_rel + (int64_t)head * D + EPU * c) * ES);
+        *reinterpret_cast<uint4*>(rsb + (r * RP + EPU * c) * ES) = v;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int k0 = 0; k0 < UB; k0 += KSTEP) {
+        const auto bop = kop_rows<T>(dsb, DP, k0, 32 * wave, lane);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) acc[db] = Ty<T>::mma(kop_rows<T>(rsb, RP, k0, 32 * db, lane), bop, acc[db]);
+      }
+      __syncthreads();
+    }
+  }
+  const int64_t t = t0 + 32 * wave + li;
+  if (t >= p.tokens) return;
+  const float* part = KSIDE ? p.dk_part : p.dq_part;
+  const float* fars = KSIDE ? p.bfar : p.afar;
+  void* outp = KSIDE ? p.dk : p.dq;
+  float fgt = 0.f, flt = 0.f;
+  int r_gt = 0, r_lt = 0;
+  if (on) {
+    fgt = fars[(t * p.H + head) * 2 + 0];
+    flt = fars[(t * p.H + head) * 2 + 1];
+    const int row_top = rel_row(p, p.rel_max_len - 1), row_bot = rel_row(p, -(p.rel_max_len - 1));
+    r_gt = KSIDE ? row_bot : row_top;
+    r_lt = KSIDE ? row_top : row_bot;
+  }
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = db * 32 + 8 * g + 4 * lh + e;
+        float a = acc[db][4 * g + e];
+        if (on) {
+          a += fgt * to_f<T>(rel, (int64_t)r_gt * p.ld_rel + (int64_t)head * D + c);
+          a += flt * to_f<T>(rel, (int64_t)r_lt * p.ld_rel + (int64_t)head * D + c);
+        }
+        from_f<T>(outp, t * ((int64_t)p.H * D) + (int64_t)head * D + c,
+                  part[(t * p.H + head) * D + c] + p.tau * a);
+      }
+}
+
+// W[h][b][u + band - 1] = sum over the tokens i of unit b of D[u][i] x_i
+// (C2P: Dq with q; P2C: Dk with k), for |u| < band. As a product
+// W [U x d] = D [U x tokens] X [tokens x d]: a workgroup owns 128 distances
+// of one (unit, head) (32 per wave) and walks the unit's tokens 32 at a
+// time from an 8-aligned start; X rows of tokens outside the unit are
+// staged as zero, so the neighbouring units' entries of D add nothing.
+template <class T, int D, bool KSIDE>
+__global__ __launch_bounds__(256) void bwd_pos_w_kernel(BwdParams p) {
+  constexpr int ES = Ty<T>::ESIZE;
+  constexpr int UB = 128, IB = 32, EPU = 16 / ES;
+  constexpr int DP = IB + 16 / ES;     // D block pitch (elements)
+  constexpr int XP = D + 32 / ES;      // X block pitch
+  constexpr int NDB = D / 32;
+  constexpr int KSTEP = ES == 2 ? 16 : 2;
+  __shared__ __attribute__((aligned(16))) unsigned char dsb[UB * DP * ES];
+  __shared__ __attribute__((aligned(16))) unsigned char xsb[IB * XP * ES];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 31, lh = lane >> 5;
   const int head = blockIdx.z, b = blockIdx.y;
+  const bool on = KSIDE ? (p.flags & 2u) != 0 : (p.flags & 1u) != 0;
+  if (!on) return;
   const int band = p.band;
   const int dg_rows = 2 * band - 1;
   const int wrows = 2 * band + 1;
-  const int row0 = blockIdx.x * RB;
+  const int row0 = blockIdx.x * UB;
   const int len = unit_len(p, b);
   const int64_t tok0 = unit_base(p, b);
-  const int64_t wbase = ((int64_t)head * p.units + b) * wrows * d;
-  const bool c2p = (p.flags & 1u) != 0, p2c = (p.flags & 2u) != 0;
-  __shared__ float aq[RB][IB + 1], ak[RB][IB + 1];
-  __shared__ float qs[IB][128 + 1], ks[IB][128 + 1];
-  const int c = threadIdx.x % d;
-  const int per = 256 / d;
-  const int rg = threadIdx.x / d;
-  constexpr int MAXR = RB / 2;   // d >= 32: at most 32 rows per thread
-  const int nr = RB / per;
-  float oq[MAXR], ok[MAXR];
+  const unsigned char* dgs = reinterpret_cast<const unsigned char*>(KSIDE ? p.dgk : p.dgq);
+  const unsigned char* xg = reinterpret_cast<const unsigned char*>(KSIDE ? p.k : p.q);
+  const int64_t ldx = KSIDE ? p.ld_k : p.ld_q;
+  float* wout = KSIDE ? p.wk : p.wq;
+
+  f32x16_t acc[NDB];
 #pragma unroll
-  for (int k = 0; k < MAXR; ++k) { oq[k] = 0.f; ok[k] = 0.f; }
-  for (int i0 = 0; i0 < len; i0 += IB) {
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x16_t{};
+  // token chunks are the 32-token groups of the store
+  const int64_t ia = tok0 & ~(int64_t)31;
+  for (int64_t i0 = ia; i0 < tok0 + len; i0 += IB) {
+    const int64_t gbase = ((int64_t)head * p.dg_groups + (i0 >> 5)) * p.dg_rows;
+    for (int x = tid; x < UB * (IB / EPU); x += 256) {
+      const int r = x / (IB / EPU), c = x - r * (IB / EPU);
+      const int row = row0 + r;   // distance row - (band - 1)
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (row < dg_rows) v = ld16(dgs + ((gbase + (row - (band - 1) + p.dg_rb)) * 32 + EPU * c) * ES);
+      *reinterpret_cast<uint4*>(dsb + (r * DP + EPU * c) * ES) = v;
+    }
+    for (int x = tid; x < IB * (D / EPU); x += 256) {
+      const int r = x / (D / EPU), c = x - r * (D / EPU);
+      const int64_t i = i0 + r;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (i >= tok0 && i < tok0 + len) v = ld16(xg + (i * ldx + (int64_t)head * D + EPU * c) * ES);
+      *reinterpret_cast<uint4*>(xsb + (r * XP + EPU * c) * ES) = v;
+    }
     __syncthreads();
-    for (int x = threadIdx.x; x < RB * IB; x += 256) {
-      const int rl = x / IB, il = x - rl * IB;
-      const int row = row0 + rl, i = i0 + il;
-      float vq = 0.f, vk = 0.f;
-      if (row < wrows && i < len) {
-        if (row < dg_rows) {
-          const int u = row - (band - 1);
-          const int64_t drow = ((int64_t)head * dg_rows + row) * p.tokens + tok0;
-          // pair (i, i - u) for q; pair (i + u, i) for k (i is then the key)
-          if (c2p && i - u >= 0 && i - u < len) vq = to_f<T>(p.dg, drow + i);
-          if (p2c && i + u >= 0 && i + u < len) vk = to_f<T>(p.dg, drow + i + u);
-        } else {
-          const int which = row - dg_rows;
-          if (c2p) vq = p.afar[((tok0 + i) * p.H + head) * 2 + which];
-          if (p2c) vk = p.bfar[((tok0 + i) * p.H + head) * 2 + which];
-        }
+#pragma unroll
+    for (int k0 = 0; k0 < IB; k0 += KSTEP) {
+      const auto aop = mop_rows<T>(dsb, DP, k0, 32 * wave, lane);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc[db] = Ty<T>::mma(aop, kop_rows<T>(xsb, XP, k0, 32 * db, lane), acc[db]);
+    }
+    __syncthreads();
+  }
+  // lane: column c = 32 db + li; registers: rows 8 g + 4 lh + e of the wave's 32
+  const int64_t wbase = ((int64_t)head * p.units + b) * wrows * D;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = row0 + 32 * wave + 8 * g + 4 * lh + e;
+        if (row < dg_rows) wout[wbase + (int64_t)row * D + 32 * db + li] = acc[db][4 * g + e];
       }
-      aq[rl][il] = vq;
-      ak[rl][il] = vk;
-    }
-    for (int x = threadIdx.x; x < IB * d; x += 256) {
-      const int il = x / d, e = x - il * d;
-      const int i = i0 + il;
-      const bool in = i < len;
-      qs[il][e] = (c2p && in) ? to_f<T>(p.q, (tok0 + i) * p.ld_q + (int64_t)head * d + e) : 0.f;
-      ks[il][e] = (p2c && in) ? to_f<T>(p.k, (tok0 + i) * p.ld_k + (int64_t)head * d + e) : 0.f;
-    }
-    __syncthreads();
-    for (int il = 0; il < IB; ++il) {
-      const float qv = qs[il][c], kv = ks[il][c];
+}
+
+// the two rows of W past the distances: sum over the unit's tokens of the
+// beyond-band sums (u >= band, then u <= -band) times q (C2P) and k (P2C).
+// One workgroup per (unit, head): a thread owns one 16-byte column group
+// and a strided subset of the tokens; the token groups are then added in a
+// fixed order.
+template <class T, int D>
+__global__ __launch_bounds__(256) void bwd_pos_farw_kernel(BwdParams p) {
+  constexpr int ES = Ty<T>::ESIZE, EPU = 16 / ES;
+  constexpr int CG = D / EPU, TG = 256 / CG;
+  const int head = blockIdx.y, b = blockIdx.x;
+  const int len = unit_len(p, b);
+  const int64_t tok0 = unit_base(p, b);
+  const int band = p.band;
+  const int wrows = 2 * band + 1;
+  const bool c2p = (p.flags & 1u) != 0, p2c = (p.flags & 2u) != 0;
+  const int cg = threadIdx.x % CG, tg = threadIdx.x / CG;
+  const unsigned char* qb = reinterpret_cast<const unsigned char*>(p.q);
+  const unsigned char* kb = reinterpret_cast<const unsigned char*>(p.k);
+  float s[4][EPU];   // q * afar_gt, q * afar_lt, k * bfar_gt, k * bfar_lt
 #pragma unroll
-      for (int k = 0; k < MAXR; ++k)
-        if (k < nr) {
-          oq[k] += aq[rg + k * per][il] * qv;
-          ok[k] += ak[rg + k * per][il] * kv;
-        }
+  for (int w = 0; w < 4; ++w)
+#pragma unroll
+    for (int e = 0; e < EPU; ++e) s[w][e] = 0.f;
+  auto unpack = [](uint4 u, float (&f)[EPU]) {
+    if constexpr (ES == 2) {
+      const auto v = __builtin_bit_cast(typename Ty<T>::frag, u);
+#pragma unroll
+      for (int e = 0; e < EPU; ++e) f[e] = (float)v[e];
+    } else {
+      const f32x4_t v = __builtin_bit_cast(f32x4_t, u);
+#pragma unroll
+      for (int e = 0; e < EPU; ++e) f[e] = v[e];
+    }
+  };
+#pragma unroll 2
+  for (int i = tg; i < len; i += TG) {
+    const int64_t t = tok0 + i;
+    float f[EPU];
+    if (c2p) {
+      unpack(ld16(qb + (t * p.ld_q + (int64_t)head * D + EPU * cg) * ES), f);
+      const float a0 = p.afar[(t * p.H + head) * 2 + 0], a1 = p.afar[(t * p.H + head) * 2 + 1];
+#pragma unroll
+      for (int e = 0; e < EPU; ++e) { s[0][e] += a0 * f[e]; s[1][e] += a1 * f[e]; }
+    }
+    if (p2c) {
+      unpack(ld16(kb + (t * p.ld_k + (int64_t)head * D + EPU * cg) * ES), f);
+      const float b0 = p.bfar[(t * p.H + head) * 2 + 0], b1 = p.bfar[(t * p.H + head) * 2 + 1];
+#pragma unroll
+      for (int e = 0; e < EPU; ++e) { s[2][e] += b0 * f[e]; s[3][e] += b1 * f[e]; }
     }
   }
+  __shared__ float red[TG][4 * D];
 #pragma unroll
-  for (int k = 0; k < MAXR; ++k) {
-    const int row = row0 + rg + k * per;
-    if (k >= nr || row >= wrows) continue;
-    p.wq[wbase + (int64_t)row * d + c] = oq[k];
-    p.wk[wbase + (int64_t)row * d + c] = ok[k];
+  for (int w = 0; w < 4; ++w)
+#pragma unroll
+    for (int e = 0; e < EPU; ++e) red[tg][w * D + EPU * cg + e] = s[w][e];
+  __syncthreads();
+  const int64_t wbase = ((int64_t)head * p.units + b) * wrows * D;
+  for (int c = threadIdx.x; c < 4 * D; c += 256) {
+    float r = 0.f;
+    for (int g = 0; g < TG; ++g) r += red[g][c];
+    const int w = c / D, col = c - w * D;
+    float* dst = w < 2 ? p.wq : p.wk;
+    dst[wbase + (int64_t)(2 * band - 1 + (w & 1)) * D + col] = r;
   }
 }
 
@@ -691,7 +1022,7 @@ __global__ __launch_bounds__(256) void bwd_pos_rel_kernel(BwdParams p, int d) {
 // ---------------------------------------------------------------------------
 
 template <class T, int D>
-int launch_main(BwdParams& p, bool varlen, hipStream_t stream) {
+int launch_t_d(BwdParams& p, bool varlen, hipStream_t stream) {
   typedef BCfg<T, D> C;
   int64_t n_work;
   if (!varlen) {
@@ -712,6 +1043,19 @@ int launch_main(BwdParams& p, bool varlen, hipStream_t stream) {
     hipLaunchKernelGGL((bwd_main_kernel<T, D, false, false>), grid, block, 0, stream, p);
     hipLaunchKernelGGL((bwd_main_kernel<T, D, true, false>), grid, block, 0, stream, p);
   }
+  const dim3 gg((unsigned)((p.tokens + 127) / 128), (unsigned)p.H);
+  hipLaunchKernelGGL((bwd_pos_grad_kernel<T, D, false>), gg, dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((bwd_pos_grad_kernel<T, D, true>), gg, dim3(256), 0, stream, p);
+  if (p.flags) {   // dkr / dqr exist only with a position term
+    const dim3 gw((unsigned)((2 * p.band - 1 + 127) / 128), (unsigned)p.units, (unsigned)p.H);
+    hipLaunchKernelGGL((bwd_pos_w_kernel<T, D, false>), gw, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((bwd_pos_w_kernel<T, D, true>), gw, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((bwd_pos_farw_kernel<T, D>), dim3((unsigned)p.units, (unsigned)p.H), dim3(256), 0, stream,
+                       p);
+    const int64_t rcells = (int64_t)p.n_rel * p.H * D;
+    hipLaunchKernelGGL(bwd_pos_rel_kernel<T>, dim3((unsigned)((rcells + 255) / 256)), dim3(256), 0, stream, p,
+                       D);
+  }
   return 0;
 }
 
@@ -720,26 +1064,21 @@ int launch_bwd_t(BwdParams& p, int d, bool varlen, hipStream_t stream) {
   const int64_t rows = p.tokens * p.H;
   hipLaunchKernelGGL(bwd_dsum_kernel<T>, dim3((unsigned)min((rows + 255) / 256 + 1, (int64_t)16384)), dim3(256),
                      0, stream, p, d);
-  int st;
   switch (d) {
-    case 32: st = launch_main<T, 32>(p, varlen, stream); break;
-    case 64: st = launch_main<T, 64>(p, varlen, stream); break;
-    case 128: st = launch_main<T, 128>(p, varlen, stream); break;
+    case 32: return launch_t_d<T, 32>(p, varlen, stream);
+    case 64: return launch_t_d<T, 64>(p, varlen, stream);
+    case 128: return launch_t_d<T, 128>(p, varlen, stream);
     default: return 2;
   }
-  if (st) return st;
-  const dim3 gg((unsigned)((p.tokens + 31) / 32), (unsigned)p.H);
-  hipLaunchKernelGGL((bwd_pos_grad_kernel<T, false>), gg, dim3(256), 0, stream, p, d);
-  hipLaunchKernelGGL((bwd_pos_grad_kernel<T, true>), gg, dim3(256), 0, stream, p, d);
-  hipLaunchKernelGGL(bwd_pos_w_kernel<T>, dim3((unsigned)((2 * p.band + 1 + 63) / 64), (unsigned)p.units, (unsigned)p.H),
-                     dim3(256), 0, stream, p, d);
-  if (p.flags) {   // dkr / dqr exist only with a position term
-    const int64_t rcells = (int64_t)p.n_rel * p.H * d;
-    hipLaunchKernelGGL(bwd_pos_rel_kernel<T>, dim3((unsigned)((rcells + 255) / 256)), dim3(256), 0, stream, p, d);
-  }
-  return 0;
 }
 
+}  // namespace
+
+namespace {
+// rows of a distance-store group: dg_rb odd and >= band - 1, then band more
+// rows, rounded up to even
+int32_t dg_rb_of(int32_t band) { return (band - 1) | 1; }
+int32_t dg_rows_of(int32_t band) { return (dg_rb_of(band) + band + 1) & ~1; }
 }  // namespace
 
 int64_t bwd_workspace_bytes(int64_t tokens, int32_t units, int32_t H, int32_t d, int esize,
@@ -747,8 +1086,9 @@ int64_t bwd_workspace_bytes(int64_t tokens, int32_t units, int32_t H, int32_t d,
   auto al = [](int64_t x) { return (x + 255) / 256 * 256; };
   const int64_t th = tokens * H;
   const int64_t wrows = 2 * (int64_t)band + 1;
-  return al(th * 4) + 2 * al(th * d * 4) + 2 * al(th * 2 * 4) +
-         al((int64_t)H * (2 * (int64_t)band - 1) * tokens * esize) + 2 * al((int64_t)H * units * wrows * d * 4);
+  const int64_t dg_bytes = al((int64_t)H * ((tokens + 31) / 32) * dg_rows_of(band) * 32 * esize);
+  return al(th * 4) + 2 * al(th * d * 4) + 2 * al(th * 2 * 4) + 2 * dg_bytes +
+         2 * al((int64_t)H * units * wrows * d * 4);
 }
 
 void bwd_carve_workspace(BwdParams& p, void* ws, int d, int esize) {
@@ -756,12 +1096,17 @@ void bwd_carve_workspace(BwdParams& p, void* ws, int d, int esize) {
   unsigned char* w = reinterpret_cast<unsigned char*>(ws);
   const int64_t th = p.tokens * p.H;
   const int64_t wrows = 2 * (int64_t)p.band + 1;
+  p.dg_groups = (p.tokens + 31) / 32;
+  p.dg_rb = dg_rb_of(p.band);
+  p.dg_rows = dg_rows_of(p.band);
+  const int64_t dg_bytes = al((int64_t)p.H * p.dg_groups * p.dg_rows * 32 * esize);
   p.dsum = reinterpret_cast<float*>(w); w += al(th * 4);
   p.dq_part = reinterpret_cast<float*>(w); w += al(th * d * 4);
   p.dk_part = reinterpret_cast<float*>(w); w += al(th * d * 4);
   p.afar = reinterpret_cast<float*>(w); w += al(th * 2 * 4);
   p.bfar = reinterpret_cast<float*>(w); w += al(th * 2 * 4);
-  p.dg = w; w += al((int64_t)p.H * (2 * (int64_t)p.band - 1) * p.tokens * esize);
+  p.dgq = w; w += dg_bytes;
+  p.dgk = w; w += dg_bytes;
   p.wq = reinterpret_cast<float*>(w); w += al((int64_t)p.H * p.units * wrows * d * 4);
   p.wk = reinterpret_cast<float*>(w);
 }

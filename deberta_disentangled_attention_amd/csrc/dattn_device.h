@@ -164,6 +164,15 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
 }
 
+// Workgroup barrier that orders LDS only: waits for this wave's LDS
+// operations (not for its outstanding global stores, which __syncthreads'
+// full fence would wait for) and synchronises the workgroup.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 // Transposing LDS read (ds_read_b64_tr_b16). In each group of 16 lanes, lane

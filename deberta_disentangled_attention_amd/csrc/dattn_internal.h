@@ -61,7 +61,14 @@ struct BwdParams {
   float* dk_part;                   // [tokens, H, d]
   float* afar;                      // [tokens, H, 2]: query-side sums, u >= band / u <= -band
   float* bfar;                      // [tokens, H, 2]: key-side sums, u >= band / u <= -band
-  void* dg;                         // [H, 2 band - 1, tokens] element type
+  // dS of the pairs closer than the band by distance u (query minus key),
+  // element type, tiled by 32-token groups: [H][groups][dg_rows][32], the
+  // entry of token t at distance u in row u + dg_rb of group t / 32
+  void* dgq;                        // token t the query: pair (t, t - u)
+  void* dgk;                        // token t the key: pair (t + u, t)
+  int64_t dg_groups;                // ceil(tokens / 32)
+  int32_t dg_rows;                  // rows per group: >= dg_rb + band, even
+  int32_t dg_rb;                    // odd, >= band - 1: the row pairs a wave writes start on 128-byte lines
   float* wq;                        // [H, units, 2 band + 1, d]: distance sums with q, then the two far sums
   float* wk;                        // [H, units, 2 band + 1, d]: with k
   int32_t n_qtiles;                 // work items per (unit, head) or tile slots (packed)
