@@ -1428,14 +1428,50 @@ int launch_inst(FwdParams& p, bool varlen, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? 0 : 3;
 }
 
+// Tile dispatch: 32 NW queries per workgroup, 64-key tiles (32 for fp32 at
+// d = 128). A sweep of NW in {2, 4, 8} over the benchmark shapes
+// (tune_tiles.py; 16-bit types) found NW = 4 fastest everywhere except
+// packed batches of short sequences, where 64-query tiles leave fewer rows
+// of a tile empty. Building with -DDATTN_NW_D32=n (D64, D128) fixes the wave
+// count of the 16-bit instances for every length: the sweep's variants.
+#if defined(DATTN_NW_D32) || defined(DATTN_NW_D64) || defined(DATTN_NW_D128)
+constexpr bool kNwForced = true;
+#else
+constexpr bool kNwForced = false;
+#endif
+#ifndef DATTN_NW_D32
+#define DATTN_NW_D32 4
+#endif
+#ifndef DATTN_NW_D64
+#define DATTN_NW_D64 4
+#endif
+#ifndef DATTN_NW_D128
+#define DATTN_NW_D128 4
+#endif
+constexpr int kShortPackedLen = 128;   // packed, max_seqlen up to this: 64-query tiles
+
 template <class T>
 int launch_dtype(FwdParams& p, int d, bool varlen, hipStream_t stream) {
+  constexpr bool h16 = Ty<T>::ESIZE == 2;
+  const bool short_packed = !kNwForced && varlen && p.max_seqlen <= kShortPackedLen;
   switch (d) {
-    case 32: return launch_inst<T, 32, 64, 4>(p, varlen, stream);
-    case 64: return launch_inst<T, 64, 64, 4>(p, varlen, stream);
+    case 32:
+      if constexpr (h16) {
+        if (short_packed) return launch_inst<T, 32, 64, 2>(p, varlen, stream);
+        return launch_inst<T, 32, 64, DATTN_NW_D32>(p, varlen, stream);
+      } else {
+        return launch_inst<T, 32, 64, 4>(p, varlen, stream);
+      }
+    case 64:
+      if constexpr (h16) {
+        if (short_packed) return launch_inst<T, 64, 64, 2>(p, varlen, stream);
+        return launch_inst<T, 64, 64, DATTN_NW_D64>(p, varlen, stream);
+      } else {
+        return launch_inst<T, 64, 64, 4>(p, varlen, stream);
+      }
     case 128:
-      if constexpr (Ty<T>::ESIZE == 4) return launch_inst<T, 128, 32, 4>(p, varlen, stream);
-      else return launch_inst<T, 128, 64, 4>(p, varlen, stream);
+      if constexpr (h16) return launch_inst<T, 128, 64, DATTN_NW_D128>(p, varlen, stream);
+      else return launch_inst<T, 128, 32, 4>(p, varlen, stream);
     default: return 2;
   }
 }

@@ -147,7 +147,9 @@ int dattn_fwd_padded(const void* q, const void* k, const void* v,
  *              behaviour, but device reads stay clamped to total_tokens.
  * max_seqlen : host-side bound on every length (<= 8192, <= rel_max_len
  *              when flags != 0). nseq, max_seqlen and total_tokens are host
- *              values, so the call needs no device-to-host read.
+ *              values, so the call needs no device-to-host read. It also
+ *              picks the tile height: 64 queries per workgroup for 16-bit
+ *              types at d <= 64 when max_seqlen <= 128, else 128.
  * out        : [total_tokens, H*d], contiguous; every row is written.
  * Other arguments as for dattn_fwd_padded.
  *

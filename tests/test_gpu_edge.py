@@ -277,3 +277,28 @@ def test_out_of_range_table_rows_read_edge_rows(dtype):
     errp = float(np.abs(gotp - workloads.pack(want, w.lens)).max())
     assert errp <= H.TOL[dtype], errp
     _say(f"clamp {dtype}: max abs err padded {worst:.3e} packed {errp:.3e}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("d", [32, 64])
+def test_short_packed_tile_dispatch(dtype, d):
+    """Packed batches whose bound max_seqlen is at most 128 run 64-query tiles;
+    the same batch under a larger bound runs the 128-query tiles. Both
+    against the oracle, with the boundary lengths 127/128 present."""
+    import torch
+    import deberta_disentangled_attention_amd as dd
+    rng = np.random.default_rng(d)
+    lens = np.concatenate([rng.integers(1, 129, size=40), [128, 127, 1, 0, 64, 65]])
+    w = workloads.make_workload("short", dtype=dtype, B=len(lens), L=128, H=3, d=d,
+                                position_buckets=32, max_relative_positions=128, lens=lens,
+                                seed=d + 1, packed=True)
+    want = H.oracle_varlen(w, rel_max_len=128)
+    cu = torch.from_numpy(w.cu_seqlens).cuda()
+    args = [H.dev(x, dtype) for x in (w.q, w.k, w.v, w.qr, w.kr)]
+    for bound in (128, 4096):
+        # the table must cover the bound; its entries depend on the distance only
+        T = H.gpu_table(bound, w.position_buckets, w.max_relative_positions)
+        got = H.host(dd.dattn_fwd_varlen(*args, T, bound, cu, bound, w.H, w.d, flags=w.flags))
+        err = float(np.abs(got - want).max())
+        print(f"short packed {dtype} d={d} bound={bound}: {err:.2e}", file=sys.stderr, flush=True)
+        assert err <= H.TOL[dtype], (bound, err)
