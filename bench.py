@@ -425,6 +425,51 @@ def bench_bwd(args):
     }), flush=True)
 
 
+def bench_fast_f32(args):
+    """Time the fast fp32 forward (fp32 in and out, products on the fp16
+    MFMA) against the strict fp32 forward on an fp32 workload; each timing
+    covers every launch of one call (the fast mode's operand conversion,
+    the fp16 kernel and the output widening)."""
+    import numpy as np
+    import torch
+    import deberta_disentangled_attention_amd as dd
+
+    w = build_workload(args.workload)
+    if w.dtype != "fp32" or w.packed:
+        raise SystemExit("--fast-f32 needs a padded fp32 workload (c1, c5f32)")
+    if args.flags is not None:
+        w.flags = args.flags
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x, np.float32)).cuda()
+    q, k, v, qr, kr = dev(w.q), dev(w.k), dev(w.v), dev(w.qr), dev(w.kr)
+    table = dd.rel_bucket(w.L, w.position_buckets, w.max_relative_positions, device="cuda")
+    mask = None if w.mask is None else torch.from_numpy(w.mask).cuda()
+    out = torch.empty((w.B, w.L, w.H * w.d), dtype=torch.float32, device="cuda")
+    need = dd.f32fast_workspace_size(w.B * w.L, w.n_rel if w.flags else 0, w.H, w.d)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+
+    def fast():
+        dd.dattn_fwd_padded_f32fast(q, k, v, qr, kr, table, w.L, mask, w.H, w.d, flags=w.flags,
+                                    out=out, workspace=ws)
+
+    def strict():
+        dd.dattn_fwd_padded(q, k, v, qr, kr, table, w.L, mask, w.H, w.d, flags=w.flags, out=out)
+
+    t_fast = _timed(fast, args.steps, args.warmup)
+    t_strict = _timed(strict, args.steps, args.warmup)
+    flop = w.effective_flop()
+    print(json.dumps({
+        "metric": "fast fp32 forward (fp16 MFMA) vs strict fp32 forward",
+        "workload": describe(w), "flags": w.flags, "steps": args.steps, "warmup": args.warmup,
+        "fast_ms": round(t_fast, 4), "strict_ms": round(t_strict, 4),
+        "speedup": round(t_strict / t_fast, 2),
+        "fast_TFLOPs": round(flop / (t_fast * 1e-3) / 1e12, 2),
+        "fast_pct_fp16_mfma_peak": round(100 * flop / (t_fast * 1e-3) / 1e12 / PEAK_TFLOPS["fp16"], 2),
+        "strict_TFLOPs": round(flop / (t_strict * 1e-3) / 1e12, 2),
+        "strict_pct_fp32_mfma_peak": round(100 * flop / (t_strict * 1e-3) / 1e12 / PEAK_TFLOPS["fp32"], 2),
+        "workspace_bytes": int(need),
+    }), flush=True)
+
+
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--write-traffic":
         write_traffic(*sys.argv[2:6])
@@ -445,6 +490,8 @@ def main():
                     help="padded forward vs the device-packed route on a padded workload")
     ap.add_argument("--relproj", action="store_true",
                     help="time the qr/kr projection of the workload's table shape")
+    ap.add_argument("--fast-f32", action="store_true",
+                    help="fast fp32 mode (fp16 MFMA) against strict fp32 on an fp32 workload")
     ap.add_argument("--bwd", action="store_true",
                     help="time the backward on the workload (forward output and lse computed once)")
     ap.add_argument("--flush-l2", action="store_true",
@@ -473,6 +520,11 @@ def main():
         return
     if args.bwd:
         bench_bwd(args)
+        return
+    if args.fast_f32:
+        if args.workload == "c4":
+            args.workload = "c5f32"
+        bench_fast_f32(args)
         return
     if args.pack:
         if args.workload == "c4":

@@ -84,6 +84,14 @@ def lib() -> ctypes.CDLL:
                                                vp, i64, i32, vp, i32, i32, vp, i32, i32, i64, vp,
                                                vp, vp, vp, vp, i32, i32, i32, u32, f32, vp]
         h.dattn_bwd_varlen_noalloc.restype = ctypes.c_int
+        h.dattn_fwd_f32fast_workspace_size.argtypes = [i64, i32, i32, i32]
+        h.dattn_fwd_f32fast_workspace_size.restype = ctypes.c_int64
+        h.dattn_fwd_padded_f32fast.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, i64, i32, vp, i32,
+                                               vp, vp, i32, i32, i32, i32, u32, f32, vp, i64, vp]
+        h.dattn_fwd_padded_f32fast.restype = ctypes.c_int
+        h.dattn_fwd_varlen_f32fast.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, i64, i32, vp, i32,
+                                               vp, i32, i32, i64, vp, i32, i32, u32, f32, vp, i64, vp]
+        h.dattn_fwd_varlen_f32fast.restype = ctypes.c_int
         h.dattn_strerror.argtypes = [ctypes.c_int]
         h.dattn_strerror.restype = ctypes.c_char_p
         _lib_handle = h
@@ -256,6 +264,84 @@ def dattn_fwd_varlen(q, k, v, qr, kr, rel_idx, rel_max_len: int, cu_seqlens, max
         float(scale), _stream(q))
     _check(st, "dattn_fwd_varlen_lse")
     return out, lse
+
+
+def f32fast_workspace_size(rows: int, n_rel: int, H: int, d: int) -> int:
+    n = lib().dattn_fwd_f32fast_workspace_size(int(rows), int(n_rel), int(H), int(d))
+    if n < 0:
+        raise ValueError("invalid sizes for the fast fp32 workspace")
+    return n
+
+
+def dattn_fwd_padded_f32fast(q, k, v, qr, kr, rel_idx, rel_max_len: int, mask, H: int, d: int,
+                             *, flags: int = DATTN_C2P | DATTN_P2C, scale: float = 0.0, out=None,
+                             workspace=None):
+    """Fast fp32 forward over a padded batch: float32 q, k, v, qr, kr; the
+    products run on the fp16 MFMA (operands rounded once to fp16)."""
+    import torch
+    B, L = q.shape[0], q.shape[1]
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32")
+        if t.shape[:2] != q.shape[:2]:
+            raise ValueError(f"{name} must match q in [B, L]")
+    lds = [_row_stride(t, n) for t, n in ((q, "q"), (k, "k"), (v, "v"))]
+    for name, t, ld in (("q", q, lds[0]), ("k", k, lds[1]), ("v", v, lds[2])):
+        if B > 1 and t.stride(0) != L * ld:
+            raise ValueError(f"{name}: batch stride must be L * row stride")
+    ld_rel, n_rel = 0, 0
+    if qr is not None:
+        if kr is None or kr.stride() != qr.stride() or kr.shape != qr.shape or qr.dtype != torch.float32:
+            raise ValueError("qr and kr must be float32 with the same shape and strides")
+        ld_rel, n_rel = _row_stride(qr, "qr"), qr.shape[0]
+    if mask is not None:
+        if mask.dtype == torch.bool:
+            mask = mask.view(torch.uint8)
+        if mask.dtype != torch.uint8 or not mask.is_contiguous() or tuple(mask.shape) != (B, L):
+            raise ValueError("mask must be a contiguous [B, L] uint8/bool tensor")
+    _table_check(rel_idx, rel_max_len, flags, q.device)
+    out = _out_tensor(out, B * L, H * d, q, lead=(B, L))
+    if workspace is None:
+        need = f32fast_workspace_size(B * L, n_rel if flags else 0, H, d)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = lib().dattn_fwd_padded_f32fast(
+        _ptr(q), _ptr(k), _ptr(v), lds[0], lds[1], lds[2], _ptr(qr), _ptr(kr), ld_rel, n_rel,
+        _ptr(rel_idx), int(rel_max_len), _ptr(mask), _ptr(out), B, L, H, d, int(flags),
+        float(scale), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q))
+    _check(st, "dattn_fwd_padded_f32fast")
+    return out
+
+
+def dattn_fwd_varlen_f32fast(q, k, v, qr, kr, rel_idx, rel_max_len: int, cu_seqlens,
+                             max_seqlen: int, H: int, d: int, *,
+                             flags: int = DATTN_C2P | DATTN_P2C, scale: float = 0.0, out=None,
+                             workspace=None):
+    """Fast fp32 forward over packed sequences (float32 operands)."""
+    import torch
+    T = q.shape[0]
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.float32 or t.shape[0] != T:
+            raise ValueError(f"{name} must be float32 with q's rows")
+    lds = [_row_stride(t, n) for t, n in ((q, "q"), (k, "k"), (v, "v"))]
+    ld_rel, n_rel = 0, 0
+    if qr is not None:
+        if kr is None or kr.stride() != qr.stride() or kr.shape != qr.shape or qr.dtype != torch.float32:
+            raise ValueError("qr and kr must be float32 with the same shape and strides")
+        ld_rel, n_rel = _row_stride(qr, "qr"), qr.shape[0]
+    if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous int32 tensor")
+    _table_check(rel_idx, rel_max_len, flags, q.device)
+    out = _out_tensor(out, T, H * d, q)
+    if workspace is None:
+        need = f32fast_workspace_size(T, n_rel if flags else 0, H, d)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = lib().dattn_fwd_varlen_f32fast(
+        _ptr(q), _ptr(k), _ptr(v), lds[0], lds[1], lds[2], _ptr(qr), _ptr(kr), ld_rel, n_rel,
+        _ptr(rel_idx), int(rel_max_len), _ptr(cu_seqlens), cu_seqlens.numel() - 1, int(max_seqlen),
+        T, _ptr(out), H, d, int(flags), float(scale), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(q))
+    _check(st, "dattn_fwd_varlen_f32fast")
+    return out
 
 
 def rel_bucket_band(max_len: int, position_buckets: int, max_relative_positions: int) -> int:

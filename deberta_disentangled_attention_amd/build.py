@@ -17,7 +17,8 @@ import sys
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_PATH = os.path.join(PKG_DIR, "libdattn.so")
-SOURCES = ["dattn_api.hip", "dattn_fwd.hip", "dattn_bwd.hip", "pack.hip", "rel_bucket.hip", "relproj.hip"]
+SOURCES = ["dattn_api.hip", "dattn_fwd.hip", "dattn_bwd.hip", "fast_f32.hip", "pack.hip", "rel_bucket.hip",
+           "relproj.hip"]
 ARCH = "gfx950"
 
 

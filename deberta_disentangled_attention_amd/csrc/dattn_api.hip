@@ -167,6 +167,116 @@ int dattn_fwd_varlen_lse(const void* q, const void* k, const void* v, int64_t ld
 }
 
 // ---------------------------------------------------------------------------
+// fast fp32 forward: operands rounded to fp16 in the workspace, the fp16
+// forward, the output widened back to fp32
+// ---------------------------------------------------------------------------
+
+}  // extern "C"
+
+namespace {
+
+int64_t al256(int64_t x) { return (x + 255) / 256 * 256; }
+
+int64_t fast_ws_bytes(int64_t rows, int32_t n_rel, int32_t H, int32_t d) {
+  const int64_t hd = (int64_t)H * d;
+  return 4 * al256(rows * hd * 2) + 2 * al256((int64_t)n_rel * hd * 2);
+}
+
+// fp16 copies of the operands in the workspace, then the fp16 forward into
+// the workspace's output rows, then those rows widened into out
+template <class Run>
+int fast_f32(const void* q, const void* k, const void* v, int64_t ld_q, int64_t ld_k, int64_t ld_v,
+             const void* qr, const void* kr, int64_t ld_rel, int32_t n_rel, uint32_t flags,
+             void* out, int64_t rows, int32_t H, int32_t d, void* workspace, int64_t workspace_bytes,
+             hipStream_t stream, Run run) {
+  if (!workspace) return DATTN_ERR_INVALID_ARGUMENT;
+  if (!aligned16(workspace)) return DATTN_ERR_UNSUPPORTED;
+  if (rows == 0) return DATTN_OK;
+  const int32_t nr = flags ? n_rel : 0;
+  if (workspace_bytes < fast_ws_bytes(rows, nr, H, d)) return DATTN_ERR_INVALID_ARGUMENT;
+  const int64_t hd = (int64_t)H * d;
+  unsigned char* w = reinterpret_cast<unsigned char*>(workspace);
+  auto take = [&](int64_t n) {
+    _Float16* p = reinterpret_cast<_Float16*>(w);
+    w += al256(n * 2);
+    return p;
+  };
+  _Float16 *q16 = take(rows * hd), *k16 = take(rows * hd), *v16 = take(rows * hd), *o16 = take(rows * hd);
+  _Float16 *qr16 = nullptr, *kr16 = nullptr;
+  dattn::F16Segs segs = {};
+  segs.seg[0] = {reinterpret_cast<const float*>(q), ld_q, q16, rows, hd};
+  segs.seg[1] = {reinterpret_cast<const float*>(k), ld_k, k16, rows, hd};
+  segs.seg[2] = {reinterpret_cast<const float*>(v), ld_v, v16, rows, hd};
+  segs.n = 3;
+  if (nr) {
+    qr16 = take((int64_t)nr * hd);
+    kr16 = take((int64_t)nr * hd);
+    segs.seg[3] = {reinterpret_cast<const float*>(qr), ld_rel, qr16, nr, hd};
+    segs.seg[4] = {reinterpret_cast<const float*>(kr), ld_rel, kr16, nr, hd};
+    segs.n = 5;
+  }
+  int st = dattn::launch_to_f16(segs, stream);
+  if (st != DATTN_OK) return st;
+  st = run(q16, k16, v16, hd, qr16, kr16, o16);
+  if (st != DATTN_OK) return st;
+  return dattn::launch_to_f32(o16, reinterpret_cast<float*>(out), rows * hd, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t dattn_fwd_f32fast_workspace_size(int64_t rows, int32_t n_rel, int32_t H, int32_t d) {
+  if (rows < 0 || n_rel < 0 || H < 1) return -1;
+  if (d != 32 && d != 64 && d != 128) return -1;
+  return fast_ws_bytes(rows, n_rel, H, d);
+}
+
+int dattn_fwd_padded_f32fast(const void* q, const void* k, const void* v, int64_t ld_q,
+                             int64_t ld_k, int64_t ld_v, const void* qr, const void* kr,
+                             int64_t ld_rel, int32_t n_rel, const int32_t* rel_idx,
+                             int32_t rel_max_len, const uint8_t* mask, void* out, int32_t B,
+                             int32_t L, int32_t H, int32_t d, uint32_t flags, float scale,
+                             void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+  if (B < 0 || L < 0) return DATTN_ERR_INVALID_ARGUMENT;
+  int st = check_common(q, k, v, ld_q, ld_k, ld_v, qr, kr, ld_rel, n_rel, rel_idx, rel_max_len,
+                        out, H, d, DATTN_F32, flags, scale, L);
+  if (st != DATTN_OK) return st;
+  return fast_f32(q, k, v, ld_q, ld_k, ld_v, qr, kr, ld_rel, n_rel, flags, out, (int64_t)B * L, H,
+                  d, workspace, workspace_bytes, stream,
+                  [&](const void* q16, const void* k16, const void* v16, int64_t hd,
+                      const void* qr16, const void* kr16, void* o16) {
+                    return fwd_padded(q16, k16, v16, hd, hd, hd, qr16, kr16, hd, n_rel, rel_idx,
+                                      rel_max_len, mask, o16, B, L, H, d, DATTN_F16, flags, scale,
+                                      nullptr, stream);
+                  });
+}
+
+int dattn_fwd_varlen_f32fast(const void* q, const void* k, const void* v, int64_t ld_q,
+                             int64_t ld_k, int64_t ld_v, const void* qr, const void* kr,
+                             int64_t ld_rel, int32_t n_rel, const int32_t* rel_idx,
+                             int32_t rel_max_len, const int32_t* cu_seqlens, int32_t nseq,
+                             int32_t max_seqlen, int64_t total_tokens, void* out, int32_t H,
+                             int32_t d, uint32_t flags, float scale, void* workspace,
+                             int64_t workspace_bytes, hipStream_t stream) {
+  if (nseq < 0 || total_tokens < 0 || max_seqlen < 0) return DATTN_ERR_INVALID_ARGUMENT;
+  if (!cu_seqlens) return DATTN_ERR_INVALID_ARGUMENT;
+  if (!aligned4(cu_seqlens)) return DATTN_ERR_UNSUPPORTED;
+  int st = check_common(q, k, v, ld_q, ld_k, ld_v, qr, kr, ld_rel, n_rel, rel_idx, rel_max_len,
+                        out, H, d, DATTN_F32, flags, scale, max_seqlen);
+  if (st != DATTN_OK) return st;
+  if (nseq == 0) return DATTN_OK;
+  return fast_f32(q, k, v, ld_q, ld_k, ld_v, qr, kr, ld_rel, n_rel, flags, out, total_tokens, H, d,
+                  workspace, workspace_bytes, stream,
+                  [&](const void* q16, const void* k16, const void* v16, int64_t hd,
+                      const void* qr16, const void* kr16, void* o16) {
+                    return fwd_varlen(q16, k16, v16, hd, hd, hd, qr16, kr16, hd, n_rel, rel_idx,
+                                      rel_max_len, cu_seqlens, nseq, max_seqlen, total_tokens, o16,
+                                      H, d, DATTN_F16, flags, scale, nullptr, stream);
+                  });
+}
+
+// ---------------------------------------------------------------------------
 // backward
 // ---------------------------------------------------------------------------
 

@@ -104,6 +104,22 @@ int launch_gather_rows(const void* src, int64_t ld_src, int64_t n_src, const int
                        int64_t n_rows, int64_t row_bytes, void* dst, int64_t ld_dst,
                        bool zero_missing, hipStream_t stream);
 
+// fp32 rows (first `cols` of each, row stride ld_src elements) -> contiguous
+// fp16 rows; cols a multiple of 4, sources 16-byte aligned
+struct F16Seg {
+  const float* src;
+  int64_t ld_src;
+  _Float16* dst;
+  int64_t rows, cols;
+};
+struct F16Segs {
+  F16Seg seg[5];
+  int n;
+};
+int launch_to_f16(const F16Segs& segs, hipStream_t stream);
+// n fp16 values (n a multiple of 4) -> fp32
+int launch_to_f32(const void* src, float* dst, int64_t n, hipStream_t stream);
+
 // qr = E Wq^T + bq, kr = E Wk^T + bk (biases may be null); strides in elements
 int launch_rel_proj(const void* E, int64_t ld_e, const void* Wq, const void* Wk, int64_t ld_w,
                     const void* bq, const void* bk, void* qr, void* kr, int64_t ld_out,

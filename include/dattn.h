@@ -198,6 +198,47 @@ int dattn_fwd_varlen_lse(const void* q, const void* k, const void* v,
                          uint32_t flags, float scale, hipStream_t stream);
 
 /*
+ * dattn_fwd_padded_f32fast, dattn_fwd_varlen_f32fast - the forward on fp32
+ * operands in the fast fp32 mode the DisentangledFlash README ("Status")
+ * lists beside strict fp32. CDNA4 has no TF32 matrix instruction; the fp16
+ * MFMA takes operands with TF32's 10-bit mantissa and accumulates in fp32.
+ * So q, k, v (and qr, kr with position terms) are rounded once to fp16
+ * (nearest even) into the workspace, the fp16 forward runs on them, and its
+ * output (rounded to fp16 like any fp16 output) is widened into the fp32
+ * out. Accuracy is that of the fp16 forward; the exponent range is fp16's
+ * (magnitudes above 65504 overflow, below 2^-24 flush to zero).
+ *
+ * Arguments as for dattn_fwd_padded / dattn_fwd_varlen with dtype fixed
+ * to fp32 (q, k, v, qr, kr, out are float), plus:
+ * workspace : device memory of at least dattn_fwd_f32fast_workspace_size()
+ *             bytes for `rows` = B*L (padded) or total_tokens (packed) and
+ *             n_rel (0 when flags == 0); 16-byte aligned, owned by the
+ *             caller, overwritten; calls that share a workspace must not
+ *             overlap.
+ * Errors: those of the fp32 forward, plus INVALID_ARGUMENT for a NULL or
+ * too small workspace, UNSUPPORTED for a misaligned one.
+ */
+int64_t dattn_fwd_f32fast_workspace_size(int64_t rows, int32_t n_rel, int32_t H, int32_t d);
+
+int dattn_fwd_padded_f32fast(const void* q, const void* k, const void* v,
+                             int64_t ld_q, int64_t ld_k, int64_t ld_v,
+                             const void* qr, const void* kr, int64_t ld_rel, int32_t n_rel,
+                             const int32_t* rel_idx, int32_t rel_max_len,
+                             const uint8_t* mask, void* out,
+                             int32_t B, int32_t L, int32_t H, int32_t d,
+                             uint32_t flags, float scale,
+                             void* workspace, int64_t workspace_bytes, hipStream_t stream);
+
+int dattn_fwd_varlen_f32fast(const void* q, const void* k, const void* v,
+                             int64_t ld_q, int64_t ld_k, int64_t ld_v,
+                             const void* qr, const void* kr, int64_t ld_rel, int32_t n_rel,
+                             const int32_t* rel_idx, int32_t rel_max_len,
+                             const int32_t* cu_seqlens, int32_t nseq, int32_t max_seqlen,
+                             int64_t total_tokens, void* out, int32_t H, int32_t d,
+                             uint32_t flags, float scale,
+                             void* workspace, int64_t workspace_bytes, hipStream_t stream);
+
+/*
  * Backward of the forward above: the gradients of a scalar loss with respect
  * to q, k, v and the relative tables qr, kr, given dout = dLoss/dout. The
  * pages' forward is inference-only (DisentangledFlash README "Status"); the

@@ -336,3 +336,32 @@ def test_noalloc_rejects_problems_beyond_its_array_before_any_hip_call():
     assert b"allocation-free" in lib.dattn_strerror(dd.DATTN_ERR_SCRATCH_TOO_SMALL)
     args[1] = None   # argument errors come first
     assert lib.dattn_bwd_varlen_noalloc(*args) == INV
+
+
+def fast_padded(**kw):
+    a = dict(q=A, k=A, v=A, ld_q=768, ld_k=768, ld_v=768, qr=A, kr=A, ld_rel=768, n_rel=512,
+             rel_idx=A, rel_max_len=512, mask=None, out=A, B=2, L=512, H=12, d=64, flags=3,
+             scale=0.0, ws=A, ws_bytes=1 << 40)
+    a.update(kw)
+    return dd.lib().dattn_fwd_padded_f32fast(
+        a["q"], a["k"], a["v"], a["ld_q"], a["ld_k"], a["ld_v"], a["qr"], a["kr"], a["ld_rel"],
+        a["n_rel"], a["rel_idx"], a["rel_max_len"], a["mask"], a["out"], a["B"], a["L"], a["H"],
+        a["d"], a["flags"], a["scale"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ws=None), INV), (dict(ws_bytes=100), INV), (dict(ws=A + 8), UNS), (dict(q=A + 4), UNS),
+    (dict(ld_q=770), UNS), (dict(d=48), UNS), (dict(L=9000), UNS), (dict(B=-1), INV),
+    (dict(out=None), INV),
+])
+def test_fast_f32_rejections(kw, status):
+    assert fast_padded(**kw) == status
+
+
+def test_fast_f32_workspace_size():
+    lib = dd.lib()
+    # q, k, v and the fp16 output rows, then the two fp16 tables
+    assert lib.dattn_fwd_f32fast_workspace_size(1024, 512, 16, 128) == 4 * 1024 * 2048 * 2 + 2 * 512 * 2048 * 2
+    assert lib.dattn_fwd_f32fast_workspace_size(1, 0, 1, 32) == 4 * 256
+    assert lib.dattn_fwd_f32fast_workspace_size(10, 0, 1, 48) == -1
+    assert fast_padded(B=0) == dd.DATTN_OK
