@@ -43,7 +43,8 @@ if ROOT not in sys.path:
 METRIC = "effective TFLOP/s + tokens/s, disentangled attn fwd, bf16 d=64, % MFMA peak"
 PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}   # MI355X dense MFMA
 HBM_GBS = 8000.0
-KERNEL_SOURCES = ["deberta_disentangled_attention_amd/csrc/dattn_fwd.hip"]
+KERNEL_SOURCES = ["deberta_disentangled_attention_amd/csrc/dattn_fwd.hip",
+                  "deberta_disentangled_attention_amd/csrc/dattn_device.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dattn_fwd_c4_bf16_traffic.json")
 
 
