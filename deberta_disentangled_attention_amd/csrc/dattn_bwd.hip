@@ -77,7 +77,9 @@ struct BCfg {
   static constexpr int OFF_R1 = 0;
   static constexpr int OFF_R2 = OFF_R1 + ROWS_BYTES;
   static constexpr int OFF_SCR = OFF_R2 + ROWS_BYTES;
-  static constexpr int OFF_XF = OFF_SCR + NW * SCR_BYTES;   // per lane: the far-block operand
+  static constexpr int CARRY_BYTES = 31 * 32 * 4;    // per wave: distance-store rows awaiting the next block
+  static constexpr int OFF_CARRY = OFF_SCR + NW * SCR_BYTES;
+  static constexpr int OFF_XF = OFF_CARRY + NW * CARRY_BYTES;   // per lane: the far-block operand
   static constexpr int OFF_STAT = OFF_XF + NT * NU * 16;
   static constexpr int OFF_MISC = OFF_STAT + 2 * BY * 4;
   static constexpr int LDS_BYTES = OFF_MISC + 64;
@@ -507,6 +509,68 @@ __global__ __launch_bounds__(256, (D <= 64 && Ty<T>::ESIZE == 2) ? 2 : 1) void b
     return fs;
   };
 
+  // The distance store is written in complete rows of the wave's 32 tokens.
+  // With block n's dS in scratch row ri = 31 + (y - y0) - li, row ri holds
+  // the distance u(ri) (Q side x0w - y0 + 31 - ri, K side y0 - x0w - 31 +
+  // ri) for the tokens li in [31 - ri, 62 - ri]; the same distance is row
+  // ri - 32 of block n+1. So rows 0..31 are complete after block n (tokens
+  // li < 31 - ri came from block n-1 through `carry`), rows 32..62 wait for
+  // block n+1 in `carry`, and after the wave's last band block they are
+  // written with zeros for the tokens no block holds. Before the first band
+  // block `carry` is zero. Rows at or beyond the band are not stored.
+  float* carry = reinterpret_cast<float*>(smem + C::OFF_CARRY + wave * C::CARRY_BYTES);
+  if (e_on)
+    for (int x4 = lane; x4 < 31 * 8; x4 += 64)
+      *reinterpret_cast<f32x4_t*>(carry + 4 * x4) = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  using DgE = typename std::conditional<ES == 2, uint16_t, float>::type;
+  DgE* const dstore = reinterpret_cast<DgE*>(KSIDE ? p.dgk : p.dgq);
+  const int64_t tw = tok0 + x0w;              // the wave's first token
+  const bool al4 = (tw & 3) == 0;             // 4-token units start on 8-byte boundaries
+  // the wave's tokens lie in groups tw/32 and tw/32 + 1: offsets from the first fit 32 bits
+  DgE* const wbase = dstore + ((int64_t)head * p.dg_groups + (tw >> 5)) * p.dg_rows * 32;
+  auto to_e = [](float v) -> DgE {
+    if constexpr (ES == 2)
+      return __builtin_bit_cast(
+          uint16_t, (typename std::conditional<std::is_same<T, TF16>::value, _Float16, __bf16>::type)v);
+    else
+      return v;
+  };
+  auto put_rows = [&](int y0, bool upper) {
+#pragma unroll 1
+    for (int k = 0; k < 4; ++k) {
+      const int j = lane + 64 * k;          // (row, 4-token unit)
+      const int ri = (upper ? 32 : 0) + (j >> 3), c = j & 7;
+      const int u = KSIDE ? y0 - x0w - 31 + ri : x0w - y0 + 31 - ri;
+      if (ri > 62 || u <= -band || u >= band) continue;
+      DgE v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int lt = 4 * c + e;
+        const bool cur = upper ? (lt <= 62 - ri) : (lt >= 31 - ri);
+        const float f = cur ? scr[ri * 32 + lt] : (upper ? 0.f : carry[ri * 32 + lt]);
+        v[e] = to_e(f);
+      }
+      const int xl = x0w + 4 * c;           // unit-local first token of the unit
+      const int tl = (int)(tw & 31) + 4 * c;  // token offset from the wave's first group
+      DgE* dst = wbase + ((tl >> 5) * p.dg_rows + (u + p.dg_rb)) * 32 + (tl & 31);
+      if (al4 && xl + 3 < len) {
+        if constexpr (ES == 2)
+          *reinterpret_cast<uint2*>(dst) = make_uint2((uint32_t)v[0] | ((uint32_t)v[1] << 16),
+                                                      (uint32_t)v[2] | ((uint32_t)v[3] << 16));
+        else
+          *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{v[0], v[1], v[2], v[3]};
+      } else {
+        // unaligned start or the unit's end: one element at a time (the
+        // group of each token found separately)
+        for (int e = 0; e < 4; ++e) {
+          if (xl + e >= len) break;
+          const int te = tl + e;
+          wbase[((te >> 5) * p.dg_rows + (u + p.dg_rb)) * 32 + (te & 31)] = v[e];
+        }
+      }
+    }
+  };
+
   // Blocks with pairs inside the band (per wave: band products gathered
   // along the diagonal, dS stored by distance), or beyond it on both sides.
   auto general_block = [&](int y0) {
@@ -573,46 +637,33 @@ __global__ __launch_bounds__(256, (D <= 64 && Ty<T>::ESIZE == 2) ? 2 : 1) void b
     grads(pm, ds);
 
     // pairs beyond the band: per-position sums; inside: the distance store
+    // (selects, not branches: an if / else-if pair here became a private
+    // two-element array indexed at run time, i.e. scratch-memory traffic)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int y = y0 + rr_of(r) + 4 * lh;
       const int u = KSIDE ? (y - x) : (x - y);   // query minus key
-      if (u >= band) far_gt += ds[r];
-      else if (u <= -band) far_lt += ds[r];
+      far_gt += u >= band ? ds[r] : 0.f;
+      far_lt += u <= -band ? ds[r] : 0.f;
     }
     if (e_on && !blk_far) {
-      // dS of this wave's pairs by query-minus-key distance u into scratch
-      // [u - umin][x], then into the store indexed by the lane's token: rows
-      // u hold consecutive tokens (lanes 0-31 write row 2k, 32-63 row 2k+1)
-      const int umin = KSIDE ? y0 - (x0w + 31) : x0w - (y0 + 31);
+      // dS of this wave's pairs into scratch row ri = 31 + (y - y0) - li,
+      // whose distance (query minus key) does not depend on the lane; then
+      // the rows complete after this block go to the store
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int yr = rr_of(r) + 4 * lh;
-        scr[(KSIDE ? yr - li + 31 : li - yr + 31) * 32 + li] = ds[r];
-      }
-      // row ui holds the pair (x, y) of this block iff ui - li (Q side) or
-      // ui + li - 31 (K side) is in [0, 31]; rows past the band, positions
-      // past the extent and lanes outside the unit write nothing
-      using E = typename std::conditional<ES == 2, uint16_t, float>::type;
-      const int64_t t = tok0 + x;
-      E* ptr = reinterpret_cast<E*>(KSIDE ? p.dgk : p.dgq) +
-               (((int64_t)head * p.dg_groups + (t >> 5)) * p.dg_rows + (umin + lh + p.dg_rb)) * 32 + (t & 31);
-      const int64_t step = 64;   // two rows
-      const bool inner = umin > -band && umin + 62 < band && y0 + C::BY <= ext;   // wave-uniform
-#pragma unroll 4
-      for (int k2 = 0; k2 < 32; ++k2, ptr += step) {
-        const int ui = 2 * k2 + lh;
-        const int yo = KSIDE ? ui + li - 31 : li + 31 - ui;   // y - y0 of the pair in row ui
-        bool ok = x_in && (unsigned)yo < 32u;
-        if (!inner) {
-          const int u = umin + ui;
-          ok = ok && u > -band && u < band && y0 + yo < ext;
+      for (int r = 0; r < 16; ++r) scr[(31 + rr_of(r) + 4 * lh - li) * 32 + li] = ds[r];
+      put_rows(y0, false);
+      const int vlo_n = vlo - C::BY, vhi_n = vhi - C::BY;   // the next block's x - y range
+      const bool next_band = y0 + C::BY < y_end && !(vlo_n >= band || vhi_n <= -band);
+      if (next_band) {
+        // rows 32..62 wait for the next block: carry row ri - 32
+        for (int x4 = lane; x4 < 31 * 8; x4 += 64) {
+          const int r = x4 >> 3, c4 = x4 & 7;
+          *reinterpret_cast<f32x4_t*>(carry + r * 32 + 4 * c4) =
+              *reinterpret_cast<const f32x4_t*>(scr + (32 + r) * 32 + 4 * c4);
         }
-        if (ok) {
-          const float v = scr[ui * 32 + li];
-          if constexpr (ES == 2) *ptr = __builtin_bit_cast(uint16_t, (typename std::conditional<std::is_same<T, TF16>::value, _Float16, __bf16>::type)v);
-          else *ptr = v;
-        }
+      } else {
+        put_rows(y0, true);   // the wave's last band block: the rest of those rows is zero
       }
     }
   };
