@@ -20,22 +20,25 @@
 //  1. dsum: D_i per row and head.
 //  2. main<Q side>: a workgroup owns 128 queries of one (sequence, head) and
 //     walks the keys in blocks of 32. It recomputes S (with the position
-//     terms, as the forward's band path: per wave E = kr-row x q and
-//     F = k x qr-row products gathered along the diagonal through LDS), P
-//     and dS, accumulates the content part of dQ (dS K) and, per query,
-//     the sums of dS over the pairs whose distance u = i - j lies beyond
-//     the band (|u| >= band, where the table is constant); the dS of pairs
-//     inside the band are stored by distance, Dg[h][u][query token].
+//     terms: beyond the band from the table's saturated rows, inside it as
+//     the forward's band path, per wave E = kr-row x q and F = k x qr-row
+//     products gathered along the diagonal through LDS), P and dS,
+//     accumulates the content part of dQ (dS K) and, per query, the sums of
+//     dS over the pairs whose distance u = i - j lies beyond the band
+//     (|u| >= band, where the table is constant); the dS of pairs inside
+//     the band go to a store indexed by (distance, query token), Dq.
 //  3. main<K side>: a workgroup owns 128 keys and walks the queries. The
 //     score is symmetric under exchanging (q, kr) with (k, qr) and i with j,
 //     so the same tile routine with those operands exchanged yields S in
-//     the key-major layout; it accumulates dV, the content part of dK and
-//     the per-key sums beyond the band.
-//  4. pos_dq / pos_dk: the position parts of dQ and dK from Dg (a
-//     distance-indexed product with the table rows) and the sums beyond
-//     the band (the table's end rows); each output row is rounded once.
-//  5. pos_w: per (sequence, head) and distance, W_u = sum_i Dg[u][i] q_i
-//     and sum_j Dg[u][j+u] k_j, plus the beyond-band sums times q or k.
+//     the key-major layout; it accumulates dV, the content part of dK, the
+//     per-key sums beyond the band and the store indexed by (distance, key
+//     token), Dk.
+//  4. pos_grad: the position parts of dQ (Dq with kr rows) and dK (Dk with
+//     qr rows) as MFMA products, plus the beyond-band sums times the
+//     table's end rows; each output row is rounded once.
+//  5. pos_w: per (sequence, head) and distance, W_u = sum_i Dq[u][i] q_i and
+//     sum_j Dk[u][j] k_j (MFMA), and (pos_farw) the beyond-band sums times
+//     q or k.
 //  6. pos_rel: dkr / dqr rows, summing W over the sequences in order and
 //     over the distances that map to each row.
 
@@ -122,7 +125,7 @@ __device__ __forceinline__ int rel_row(const BwdParams& p, int dist) {
 }
 
 // ---------------------------------------------------------------------------
-// 1. D_i = dO_i . O_i; also clears the distance-indexed dS store
+// 1. D_i = dO_i . O_i
 // ---------------------------------------------------------------------------
 
 template <class T>
@@ -140,18 +143,6 @@ __global__ __launch_bounds__(256) void bwd_dsum_kernel(BwdParams p, int d) {
     float acc = 0.f;
     for (int e = 0; e < d; e += EPU) acc += dot16<T>(ld16(a + e * Ty<T>::ESIZE), ld16(b + e * Ty<T>::ESIZE));
     p.dsum[idx] = acc;
-  }
-  // zero the distance stores: entries of pairs outside every sequence are
-  // never written
-  if (p.flags) {
-    const int64_t units16 = (int64_t)p.H * p.dg_groups * p.dg_rows * 32 * Ty<T>::ESIZE / 16;
-    uint4* zq = reinterpret_cast<uint4*>(p.dgq);
-    uint4* zk = reinterpret_cast<uint4*>(p.dgk);
-    const uint4 z = make_uint4(0, 0, 0, 0);
-    for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < units16; x += stride) {
-      zq[x] = z;
-      zk[x] = z;
-    }
   }
 }
 
@@ -284,8 +275,37 @@ __global__ __launch_bounds__(256, (D <= 64 && Ty<T>::ESIZE == 2) ? 2 : 1) void b
       fs[(t * p.H + head) * 2 + 1] = 0.f;
     }
   };
+  // The distance store has no global clear: every in-band row of every
+  // token of the unit is written by the wave that owns the token, by the
+  // band blocks (put_rows below) or here, with zeros for the distances
+  // outside [ulo, uhi] (ulo > uhi: all of them), whose pairs do not exist.
+  const bool dg_on = KSIDE ? (p.flags & 2u) != 0 : (p.flags & 1u) != 0;
+  auto zero_rows = [&](int ulo, int uhi) {
+    using ZE = typename std::conditional<Ty<T>::ESIZE == 2, uint2, f32x4_t>::type;
+    const int64_t tw0 = tok0 + x0w;
+    unsigned char* base = reinterpret_cast<unsigned char*>(KSIDE ? p.dgk : p.dgq) +
+                          ((int64_t)head * p.dg_groups + (tw0 >> 5)) * p.dg_rows * 32 * Ty<T>::ESIZE;
+    const int nrows = 2 * p.band - 1;
+    for (int j = lane; j < nrows * 8; j += 64) {
+      const int u = j / 8 - (p.band - 1), c = j & 7;   // (distance, 4-token unit)
+      if (u >= ulo && u <= uhi) continue;
+      const int xl = x0w + 4 * c;
+      const int tl = (int)(tw0 & 31) + 4 * c;
+      if (((tw0 & 3) == 0) && xl + 3 < len) {
+        *reinterpret_cast<ZE*>(base + (((tl >> 5) * p.dg_rows + (u + p.dg_rb)) * 32 + (tl & 31)) * Ty<T>::ESIZE) = ZE{};
+      } else {
+        for (int e = 0; e < 4 && xl + e < len; ++e) {
+          const int te = tl + e;
+          unsigned char* q = base + (((te >> 5) * p.dg_rows + (u + p.dg_rb)) * 32 + (te & 31)) * Ty<T>::ESIZE;
+          if constexpr (Ty<T>::ESIZE == 2) *reinterpret_cast<uint16_t*>(q) = 0;
+          else *reinterpret_cast<float*>(q) = 0.f;
+        }
+      }
+    }
+  };
   if (x0 >= ext) {   // uniform: no position of this tile takes part
     write_zero_row();
+    if (dg_on && x0w < len) zero_rows(1, 0);
     return;
   }
 
@@ -716,6 +736,19 @@ __global__ __launch_bounds__(256, (D <= 64 && Ty<T>::ESIZE == 2) ? 2 : 1) void b
     else far_lt += fs;
   }
 
+  // rows of the distance store no band block of this wave covered
+  if (dg_on && x0w < len) {
+    // band blocks: y0 in (x0w - 31 - band, x0w + 31 + band), 0 <= y0 < ext
+    int y_first = x0w - 31 - band < 0 ? 0 : ((x0w - 31 - band) / C::BY + 1) * C::BY;
+    int y_last = min((nb - 1) * C::BY, ((x0w + 30 + band) / C::BY) * C::BY);
+    int ulo = 1, uhi = 0;
+    if (x0w < ext && y_first <= y_last) {
+      ulo = KSIDE ? y_first - x0w - 31 : x0w - y_last - 31;
+      uhi = KSIDE ? y_last - x0w + 31 : x0w - y_first + 31;
+    }
+    zero_rows(ulo, uhi);
+  }
+
   // ---- epilogue --------------------------------------------------------------
   const float fgt = far_gt + __shfl_xor(far_gt, 32);   // both lane halves of position x
   const float flt = far_lt + __shfl_xor(far_lt, 32);
@@ -811,36 +844,60 @@ __global__ __launch_bounds__(256) void bwd_pos_grad_kernel(BwdParams p) {
   f32x16_t acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16_t{};
+  // D rows u0 .. u0+31 over tokens t0 .. t0+127 (four 32-token groups;
+  // groups past the last token and rows past the band read as zero) and
+  // the table rows these distances read, as 16-byte units: loaded into
+  // registers one step ahead, stored to LDS when the step's turn comes
+  constexpr int ND = (UB * (TB / EPU) + 255) / 256, NR = (UB * (D / EPU) + 255) / 256;
+  uint4 pd[ND], pr[NR];
+  auto fetch = [&](int u0) {
+#pragma unroll
+    for (int k = 0; k < ND; ++k) {
+      const int x = tid + 256 * k;
+      const int r = x / (TB / EPU), c = x - r * (TB / EPU);
+      const int u = u0 + r;
+      const int64_t g = (t0 >> 5) + c / (32 / EPU);
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (x < UB * (TB / EPU) && u < band && g < p.dg_groups)
+        v = ld16(dgs + ((((int64_t)head * p.dg_groups + g) * p.dg_rows + (u + p.dg_rb)) * 32 +
+                        EPU * (c % (32 / EPU))) * ES);
+      pd[k] = v;
+    }
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+      const int x = tid + 256 * k;
+      const int r = x / (D / EPU), c = x - r * (D / EPU);
+      const int u = u0 + r;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (x < UB * (D / EPU) && u < band)
+        v = ld16(rel + ((int64_t)rel_row(p, KSIDE ? -u : u) * p.ld_rel + (int64_t)head * D + EPU * c) * ES);
+      pr[k] = v;
+    }
+  };
   if (on) {
+    fetch(-(band - 1));
     for (int u0 = -(band - 1); u0 < band; u0 += UB) {
-      // D rows u0 .. u0+31 over tokens t0 .. t0+127: four 32-token groups
-      // (groups past the last token and rows past the band read as zero)
-      for (int x = tid; x < UB * (TB / EPU); x += 256) {
+#pragma unroll
+      for (int k = 0; k < ND; ++k) {
+        const int x = tid + 256 * k;
         const int r = x / (TB / EPU), c = x - r * (TB / EPU);
-        const int u = u0 + r;
-        const int64_t g = (t0 >> 5) + c / (32 / EPU);
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (u < band && g < p.dg_groups)
-          v = ld16(dgs + ((((int64_t)head * p.dg_groups + g) * p.dg_rows + (u + p.dg_rb)) * 32 +
-                          EPU * (c % (32 / EPU))) * ES);
-        *reinterpret_cast<uint4*>(dsb + (r * DP + EPU * c) * ES) = v;
+        if (x < UB * (TB / EPU)) *reinterpret_cast<uint4*>(dsb + (r * DP + EPU * c) * ES) = pd[k];
       }
-      // the table rows these distances read
-      for (int x = tid; x < UB * (D / EPU); x += 256) {
+#pragma unroll
+      for (int k = 0; k < NR; ++k) {
+        const int x = tid + 256 * k;
         const int r = x / (D / EPU), c = x - r * (D / EPU);
-        const int u = u0 + r;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (u < band) v = ld16(rel + ((int64_t)rel_row(p, KSIDE ? -u : u) * p.ld_rel + (int64_t)head * D + EPU * c) * ES);
-        *reinterpret_cast<uint4*>(rsb + (r * RP + EPU * c) * ES) = v;
+        if (x < UB * (D / EPU)) *reinterpret_cast<uint4*>(rsb + (r * RP + EPU * c) * ES) = pr[k];
       }
-      __syncthreads();
+      lds_barrier();
+      if (u0 + UB < band) fetch(u0 + UB);
 #pragma unroll
       for (int k0 = 0; k0 < UB; k0 += KSTEP) {
         const auto bop = kop_rows<T>(dsb, DP, k0, 32 * wave, lane);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) acc[db] = Ty<T>::mma(kop_rows<T>(rsb, RP, k0, 32 * db, lane), bop, acc[db]);
       }
-      __syncthreads();
+      lds_barrier();
     }
   }
   const int64_t t = t0 + 32 * wave + li;
@@ -916,8 +973,24 @@ __global__ __launch_bounds__(256) void bwd_pos_w_kernel(BwdParams p) {
     for (int x = tid; x < UB * (IB / EPU); x += 256) {
       const int r = x / (IB / EPU), c = x - r * (IB / EPU);
       const int row = row0 + r;   // distance row - (band - 1)
+      // tokens of the group outside this sequence: their entries belong to
+      // the neighbouring sequences or to no token, so they are masked here
+      const int64_t i = i0 + EPU * c;
+      const int lo = (int)max((int64_t)0, tok0 - i), hi = (int)min((int64_t)EPU, tok0 + len - i);
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (row < dg_rows) v = ld16(dgs + ((gbase + (row - (band - 1) + p.dg_rb)) * 32 + EPU * c) * ES);
+      if (row < dg_rows && lo < hi) {
+        v = ld16(dgs + ((gbase + (row - (band - 1) + p.dg_rb)) * 32 + EPU * c) * ES);
+        if (lo > 0 || hi < EPU) {
+          uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e = 0; e < EPU; ++e) {
+            if (e >= lo && e < hi) continue;
+            if constexpr (ES == 2) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+            else w[e] = 0u;
+          }
+          v = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+      }
       *reinterpret_cast<uint4*>(dsb + (r * DP + EPU * c) * ES) = v;
     }
     for (int x = tid; x < IB * (D / EPU); x += 256) {

@@ -341,7 +341,7 @@ int dattn_bwd_varlen(const void* q, const void* k, const void* v,
  * in dattn_bwd_varlen, and the outputs are identical to its outputs.
  *
  * Every call on one GPU shares that GPU's array and leaves its contents
- * behind (the call clears what must start at zero itself): two calls that
+ * behind (no call reads a cell it has not written first): two calls that
  * overlap on one GPU, on different streams or host threads, race and give
  * wrong results. Serialise them.
  *

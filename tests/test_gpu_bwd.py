@@ -174,3 +174,54 @@ def test_bwd_c2_shape_and_determinism():
     _, g2 = run_bwd_padded(w, 3, dout)
     for name, a, b in zip(NAMES, g1, g2):
         assert torch.equal(a, b), f"{name} differs between two calls"
+
+
+@pytest.mark.parametrize("layout", ["padded", "varlen"])
+def test_bwd_workspace_prefilled_with_nan(layout):
+    """The backward clears nothing globally: every workspace cell it reads is
+    written first in the same call. A workspace full of NaN bytes must give
+    the oracle's gradients (a read of an unwritten cell would spread NaN)."""
+    import torch
+    import deberta_disentangled_attention_amd as dd
+    dt = "bf16"
+    if layout == "padded":
+        w = workloads.make_workload("nanws_p", dtype=dt, B=3, L=300, H=2, d=64, position_buckets=16,
+                                    max_relative_positions=64, lens=np.array([300, 123, 7]), seed=21)
+        rng = np.random.default_rng(5)
+        m = (rng.random((3, 300)) < 0.8).astype(np.uint8)
+        m[:, 0] = 1
+        m[1, 123:] = 0
+        m[2, 7:] = 0
+        w.mask = m
+    else:
+        w = workloads.make_workload("nanws_v", dtype=dt, B=5, L=333, H=2, d=64, position_buckets=16,
+                                    max_relative_positions=64, lens=np.array([5, 333, 0, 61, 200]),
+                                    seed=22, packed=True)
+    dout = _dout(w, 9)
+    rel = w.L if layout == "padded" else w.max_seqlen
+    band = dd.rel_bucket_band(rel, w.position_buckets, w.max_relative_positions)
+    rows = w.B * w.L if layout == "padded" else w.total_tokens
+    need = dd.bwd_workspace_size(rows, w.B, w.H, w.d, torch.bfloat16, band)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")   # NaN in every format
+    Tg = H.gpu_table(rel, w.position_buckets, w.max_relative_positions)
+    q, k, v = H.dev(w.q, dt), H.dev(w.k, dt), H.dev(w.v, dt)
+    qr, kr = H.dev(w.qr, dt), H.dev(w.kr, dt)
+    if layout == "padded":
+        mask = torch.from_numpy(np.ascontiguousarray(w.mask, np.uint8)).cuda()
+        out, lse = dd.dattn_fwd_padded(q, k, v, qr, kr, Tg, rel, mask, w.H, w.d, lse=True)
+        g = dd.dattn_bwd_padded(q, k, v, out, H.dev(dout, dt), lse, qr, kr, Tg, rel, band, mask,
+                                w.H, w.d, workspace=ws)
+        want = oracle_bwd_padded(w, 3, dout)
+    else:
+        cu = torch.from_numpy(w.cu_seqlens).cuda()
+        out, lse = dd.dattn_fwd_varlen(q, k, v, qr, kr, Tg, rel, cu, w.max_seqlen, w.H, w.d, lse=True)
+        g = dd.dattn_bwd_varlen(q, k, v, out, H.dev(dout, dt), lse, qr, kr, Tg, rel, band, cu,
+                                w.max_seqlen, w.H, w.d, workspace=ws)
+        want = oracle_bwd_varlen(w, 3, dout)
+    torch.cuda.synchronize()
+    got = {name: H.host(t) for name, t in zip(NAMES, g)}
+    if layout == "padded":
+        for name in ("dq", "dk", "dv"):
+            got[name] = got[name].reshape(w.B, w.L, w.H * w.d)
+    errs = _compare(got, want, dt, f"nan workspace {layout}", 3)
+    _say(f"nan-prefilled workspace {layout}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
