@@ -225,3 +225,20 @@ def test_bwd_workspace_prefilled_with_nan(layout):
             got[name] = got[name].reshape(w.B, w.L, w.H * w.d)
     errs = _compare(got, want, dt, f"nan workspace {layout}", 3)
     _say(f"nan-prefilled workspace {layout}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_bwd_long_sequences_real_buckets(dtype):
+    """DeBERTa's 256/512 buckets (band 512) on sequences long enough that
+    every block range occurs: workgroups whose keys lie all beyond the band
+    below, band blocks, all beyond above; packed with an odd offset."""
+    lens = np.array([1500, 2100, 3])
+    w = workloads.make_workload(f"bwd_long_{dtype}", dtype=dtype, B=len(lens), L=2100, H=2, d=64,
+                                position_buckets=256, max_relative_positions=512, lens=lens,
+                                seed=31, packed=True, qkv_scale=0.125)
+    dout = _dout(w, 13)
+    _say(f"bwd long sequences {dtype}")
+    got, _ = run_bwd_varlen(w, 3, dout)
+    want = oracle_bwd_varlen(w, 3, dout)
+    errs = _compare(got, want, dtype, f"long {dtype}", 3)
+    _say("   " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
