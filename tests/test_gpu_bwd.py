@@ -242,3 +242,32 @@ def test_bwd_long_sequences_real_buckets(dtype):
     want = oracle_bwd_varlen(w, 3, dout)
     errs = _compare(got, want, dtype, f"long {dtype}", 3)
     _say("   " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_bwd_masked_rows_and_single_tokens(dtype):
+    """A fully masked batch row (log-sum-exp -inf: zero gradients), a row
+    whose only valid token is the last one, and a one-token packed
+    sequence next to an empty one."""
+    w = workloads.make_workload(f"bwd_edge_{dtype}", dtype=dtype, B=3, L=65, H=2, d=32,
+                                position_buckets=16, max_relative_positions=64,
+                                lens=np.array([65, 65, 65]), seed=3)
+    m = np.ones((3, 65), np.uint8)
+    m[1, :] = 0
+    m[2, :64] = 0
+    w.mask = m
+    dout = _dout(w, 4)
+    got, _ = run_bwd_padded(w, 3, dout)
+    want = oracle_bwd_padded(w, 3, dout)
+    errs = _compare(got, want, dtype, f"edge padded {dtype}", 3)
+    for name in ("dq", "dk", "dv"):
+        assert np.all(got[name][1] == 0.0), f"{name}: fully masked row not zero"
+        assert np.all(got[name][2][:64] == 0.0), f"{name}: masked positions not zero"
+    wv = workloads.make_workload(f"bwd_edge_v_{dtype}", dtype=dtype, B=3, L=40, H=2, d=32,
+                                 position_buckets=16, max_relative_positions=64,
+                                 lens=np.array([1, 0, 40]), seed=5, packed=True)
+    dv_ = _dout(wv, 6)
+    gotv, _ = run_bwd_varlen(wv, 3, dv_)
+    wantv = oracle_bwd_varlen(wv, 3, dv_)
+    errs.update({k + "_v": v for k, v in _compare(gotv, wantv, dtype, f"edge varlen {dtype}", 3).items()})
+    _say(f"bwd edges {dtype}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
