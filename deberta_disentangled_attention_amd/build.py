@@ -29,22 +29,22 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libdattn.so)")
 
 
-def compile_command(out: str = LIB_PATH, extra=()) -> list:
+def _flags(extra=()) -> list:
     return [
-        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-Wall", "-Wno-unused-command-line-argument",
         f"-I{os.path.join(PKG_DIR, '..', 'include')}",
         *extra,
-        "-o", out,
-        *[os.path.join(CSRC, s) for s in SOURCES],
     ]
 
 
-def build(verbose: bool = True, out: str = LIB_PATH, extra=()) -> str:
-    """Compile the library (always recompiles) and return its path."""
-    tmp = out + ".tmp"
-    cmd = compile_command(tmp, extra)
+def compile_command(out: str = LIB_PATH, extra=()) -> list:
+    """One hipcc command that compiles and links every source (reference form)."""
+    return [hipcc(), *_flags(extra), "-shared", "-o", out, *[os.path.join(CSRC, s) for s in SOURCES]]
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -53,6 +53,26 @@ def build(verbose: bool = True, out: str = LIB_PATH, extra=()) -> str:
     err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
+    return err
+
+
+def build(verbose: bool = True, out: str = LIB_PATH, extra=()) -> str:
+    """Compile the library (always recompiles) and return its path.
+
+    Each source is compiled to an object of its own, in parallel, then the
+    objects are linked into the shared library."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    objdir = os.path.join(PKG_DIR, "_build", os.path.basename(out) + ".objs")
+    os.makedirs(objdir, exist_ok=True)
+    objs = [os.path.join(objdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+    cmds = [[hipcc(), *_flags(extra), "-c", "-o", o, os.path.join(CSRC, s)] for s, o in zip(SOURCES, objs)]
+    jobs = max(1, min(len(cmds), os.cpu_count() or 1, 16))
+    with ThreadPoolExecutor(jobs) as ex:
+        errs = list(ex.map(lambda c: _run(c, verbose), cmds))
+    tmp = out + ".tmp"
+    errs.append(_run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose))
+    err = "\n".join(e for e in errs if e.strip())
     if verbose and err.strip():
         print(err, file=sys.stderr)
     os.replace(tmp, out)

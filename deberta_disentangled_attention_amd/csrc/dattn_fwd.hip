@@ -1229,97 +1229,203 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int item, unsigned 
     // in ring slot n % NSTAGE. Loads run three tiles ahead and are waited for
     // two steps after they are issued; one barrier per tile publishes them.
     // On far tiles the P2C term is k_j . qr[row] with one saturated row per
-    // side, so it joins the Q.K product: the B operand is q_i + qr[row]
-    // (formed in fp32, rounded once to the element type), and one MFMA chain
-    // yields q_i.k_j + k_j.qr[row].
+    // side, so it joins the Q.K product, and the softmax scale joins it too:
+    // the B operand is (q_i + qr[row]) * tau * log2(e) (formed in fp32,
+    // rounded once to the element type; q_i * tau * log2(e) without P2C),
+    // and the MFMA chain starts from a per-lane bias block holding
+    // a_i tau log2(e) - m_run, so it yields the exponent of the softmax
+    // weight directly: no per-score arithmetic precedes the exponential.
     const int nfar = FL + max(tm - FR, 0);
     if (nfar > 0) {
-      auto far_tile = [&](int n) { return n < FL ? n : FR + (n - FL); };
+      const float tl2 = p.scale_log2;
       // tile n in ring slot n % NSTAGE: its K tile, then its V tile
-      auto kslot = [&](int n) { return smem + (n % C::NSTAGE) * C::SLOT_BYTES; };
+      static_assert((C::NSTAGE & (C::NSTAGE - 1)) == 0, "ring slots: a power of two");
+      auto ring_slot = [](int n) { return (uint32_t)n & (C::NSTAGE - 1); };   // n >= 0
+      auto kslot = [&](int n) { return smem + ring_slot(n) * C::SLOT_BYTES; };
       auto vslot = [&](int n) { return kslot(n) + C::KT_BYTES; };
+      // Tiles are issued in order n = 0, 1, ..., so their sources follow
+      // running pointers: one tile apart, with a jump over the general
+      // tiles [FL, FR) when the right-hand run starts.
+      const int64_t kstep = (int64_t)BN * p.ld_k * ES, vstep = (int64_t)BN * p.ld_v * ES;
+      const int64_t kjump = (int64_t)(FR - FL) * kstep, vjump = (int64_t)(FR - FL) * vstep;
+      const unsigned char* kt_nx = Kg + base * p.ld_k * ES;
+      const unsigned char* vt_nx = Vg + base * p.ld_v * ES;
+      const uint32_t wring = (uint32_t)__builtin_amdgcn_readfirstlane((int)(ring + 1024 * wave * DPW));
       auto issue = [&](int n) {
-        const int64_t j0 = far_tile(n) * BN;
-        const unsigned char* kt = Kg + (base + j0) * p.ld_k * ES;
-        const unsigned char* vt = Vg + (base + j0) * p.ld_v * ES;
-        const uint32_t slot = ring + (n % C::NSTAGE) * C::SLOT_BYTES + 1024 * wave * DPW;
+        if (__builtin_expect(n == FL, 0)) { kt_nx += kjump; vt_nx += vjump; }
+        const uint32_t slot = wring + ring_slot(n) * C::SLOT_BYTES;
 #pragma unroll
-        for (int x = 0; x < DPW; ++x) dma16(slot + 1024 * x, kt, kdo[x]);
+        for (int x = 0; x < DPW; ++x) dma16(slot + 1024 * x, kt_nx, kdo[x]);
 #pragma unroll
-        for (int x = 0; x < DPW; ++x) dma16(slot + C::KT_BYTES + 1024 * x, vt, vdo[x]);
+        for (int x = 0; x < DPW; ++x) dma16(slot + C::KT_BYTES + 1024 * x, vt_nx, vdo[x]);
+        kt_nx += kstep;
+        vt_nx += vstep;
       };
-      // q_i + qr[row] (which: 0 top row, 1 bottom row) in this lane's layout
-      auto q_plus = [&](int which, uint4 (&dst)[NU]) {
-        uint4 rf[NU];
-        lds_half_row<NU>(rf, Rrows + which * D * ES + lh * C::HALF * ES);
+      // (q_i + qr[row]) tau log2(e) (which: 0 top row, 1 bottom row, -1 no
+      // row) in this lane's layout. q_i is read again from global memory (a
+      // cache hit) rather than kept live through the far loop.
+      auto q_scaled = [&](int which, uint4 (&dst)[NU]) {
+        uint4 rf[NU], qg[NU];
+        const int qi = i0w + li;
+        if (qi < ext) {
+          load_half_row<NU>(qg, Qg + ((base + qi) * p.ld_q + hoff + lh * C::HALF) * ES);
+        } else {
+#pragma unroll
+          for (int x = 0; x < NU; ++x) qg[x] = make_uint4(0, 0, 0, 0);
+        }
+        if (which >= 0) lds_half_row<NU>(rf, Rrows + which * D * ES + lh * C::HALF * ES);
 #pragma unroll
         for (int x = 0; x < NU; ++x) {
-          const auto a = __builtin_bit_cast(typename Ty<T>::frag, qf[x]);
+          const auto a = __builtin_bit_cast(typename Ty<T>::frag, qg[x]);
           const auto b = __builtin_bit_cast(typename Ty<T>::frag, rf[x]);
-          f32x8_t sum;
+          f32x8_t v;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) sum[e] = (float)a[e] + (float)b[e];
-          dst[x] = __builtin_bit_cast(uint4, Ty<T>::cvt8(sum));
+          for (int e = 0; e < 8; ++e) v[e] = ((float)a[e] + (which >= 0 ? (float)b[e] : 0.f)) * tl2;
+          dst[x] = __builtin_bit_cast(uint4, Ty<T>::cvt8(v));
         }
+      };
+      // accumulator start of every score block: a_i tau log2(e) - m_run
+      // (m_run taken as 0 before the first offset is set)
+      float off_run = 0.f;
+      f32x16_t bias;
+      auto set_bias = [&] {
+        const float b = off_run - (m_run == NEG_INF ? 0.f : m_run);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) bias[r] = b;
       };
 
       // Software-pipelined: the scores of tile n+1 are produced by MFMAs
       // issued in the same block as tile n's exponentials.
+      // The two key blocks' MFMA chains are interleaved, so no MFMA waits
+      // for the result of the one issued just before it.
       auto scores = [&](int n, const uint4 (&qop)[NU], f32x16_t (&s)[C::NKB]) {
         const unsigned char* ks = kslot(n);
+        uint4 kf[C::NKB][NU];
 #pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb) {
-          uint4 kf[NU];
-          k_operand(ks, kb, kf);
-          s[kb] = mma_chain<T, NU, NC>(kf, qop, f32x16_t{});
-        }
+        for (int kb = 0; kb < C::NKB; ++kb) k_operand(ks, kb, kf[kb]);
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb) s[kb] = bias;
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+          for (int kb = 0; kb < C::NKB; ++kb)
+            s[kb] = Ty<T>::mma(frag_at<T, NU>(kf[kb], c), frag_at<T, NU>(qop, c), s[kb]);
       };
-      // tile n: scores in s_cur; produces the scores of tile n+1 in s_nxt
+      // P = exp2(s - sub) rounded to the element type, into pf; returns
+      // this lane's sum of the rounded P (sub only on the cold path)
+      auto exps = [&](f32x16_t (&s)[C::NKB], PFrag& pf, auto cold, float sub) -> float {
+        float ps4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+          for (int c2 = 0; c2 < 2; ++c2) {
+            f32x8_t e8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              float x = s[kb][8 * c2 + e];
+              if constexpr (decltype(cold)::value) x -= sub;
+              e8[e] = __builtin_amdgcn_exp2f(x);
+            }
+            pf[kb][c2] = Ty<T>::cvt8(e8);
+            const uint4 w = __builtin_bit_cast(uint4, pf[kb][c2]);
+            ps4[0] = Ty<T>::sum2(w.x, ps4[0]);
+            ps4[1] = Ty<T>::sum2(w.y, ps4[1]);
+            ps4[2] = Ty<T>::sum2(w.z, ps4[2]);
+            ps4[3] = Ty<T>::sum2(w.w, ps4[3]);
+          }
+        return (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
+      };
+      // tile n: scores in s_cur; produces the scores of tile n+1 in s_nxt.
+      // The offset m_run is raised only when a tile's maximum exceeds it by
+      // more than 8; the exponentials are taken against the current offset
+      // and their row-half sum (at most 32 * 2^8 when no raise is due)
+      // detects a due raise or an overflow. That rare case, and a lane with
+      // no offset yet, forms the tile's scores again from the ring, raises
+      // the offset, redoes the exponentials and moves the next tile's
+      // scores (formed with the old offset) to the new one.
+      // Returns true when it raised the offset: the bias block is then out of
+      // date, and so are the scores of tile n+1 formed here.
       auto step = [&](int n, const uint4 (&qop)[NU], f32x16_t (&s_cur)[C::NKB],
-                      f32x16_t (&s_nxt)[C::NKB]) {
+                      f32x16_t (&s_nxt)[C::NKB]) -> bool {
         const bool more = n + C::NSTAGE - 1 < nfar;
         if (more) issue(n + C::NSTAGE - 1);   // into the slot of tile n-1
-        const float a_off = has_c2p ? (far_tile(n) < FL ? a_top : a_bot) : 0.f;
-        softmax_pv_mid(
-            s_cur, a_off, vop_slot(vslot(n)),
-            // unconditional, so the MFMAs share a block with the exponentials;
-            // past the last tile of a run they read a slot whose result is
-            // not used
-            [&] { scores(n + 1, qop, s_nxt); },
-            [&](f32x16_t (&sr)[C::NKB]) { scores(n, qop, sr); });
+        PFrag pf;
+        // unconditional, so the MFMAs share a block with the exponentials;
+        // past the last tile of a run they read a slot whose result is not
+        // used
+        scores(n + 1, qop, s_nxt);
+        float ps = exps(s_cur, pf, std::false_type{}, 0.f);
+        bool raised = false;
+        if (__builtin_expect(__any(!(ps <= 32.f * 256.f) || m_run == NEG_INF), 0)) {
+          scores(n, qop, s_cur);
+          float mx4[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
+#pragma unroll
+          for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; r += 4) {
+              mx4[0] = fmaxf(mx4[0], s_cur[kb][r]);
+              mx4[1] = fmaxf(mx4[1], s_cur[kb][r + 1]);
+              mx4[2] = fmaxf(mx4[2], s_cur[kb][r + 2]);
+              mx4[3] = fmaxf(mx4[3], s_cur[kb][r + 3]);
+            }
+          const float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
+          const float mxf = fmaxf(mx, wave_xor32(mx));   // relative to the current offset
+          const float m_eff = m_run == NEG_INF ? 0.f : m_run;
+          const bool raise = m_run == NEG_INF || mxf > 8.f;
+          const float m_new = raise ? m_eff + mxf : m_run;
+          // m_run == -inf: nothing accumulated yet, alpha = exp2(-inf) = 0
+          const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+          l_part *= alpha;
+#pragma unroll
+          for (int x = 0; x < C::NDB; ++x) o_acc[x] *= alpha;
+          const float delta = m_new - m_eff;   // 0 without a raise
+          m_run = m_new;
+          ps = exps(s_cur, pf, std::true_type{}, delta);
+          raised = __any(raise);
+        }
+        l_part += ps;
+        pv_acc(pf, s_cur, vop_slot(vslot(n)));
         // tile n+2, read from the next step on, has landed once at most the
         // loads of tile n+3 are in flight; after the barrier it is visible
         // and the slot of tile n is free
         if (more) wait_vm<2 * DPW>();
         else wait_vm<0>();
         __syncthreads();
+        return raised;
       };
-      // tiles n0 .. n1-1 with B operand qop
-      auto run = [&](int n0, int n1, const uint4 (&qop)[NU]) {
-        if (n0 >= n1) return;
-        f32x16_t sa[C::NKB], sb[C::NKB];
-        scores(n0, qop, sa);
+      // tiles n0 .. n1-1 with B operand qop and C2P constant a_off. The bias
+      // block is constant inside the inner loop; a raise of the offset
+      // leaves it, and the outer loop forms the next tile's scores again
+      // with the new bias.
+      auto run = [&](int n0, int n1, const uint4 (&qop)[NU], float a_off) {
+        off_run = a_off * tl2;
         int n = n0;
-        for (; n + 1 < n1; n += 2) {
-          step(n, qop, sa, sb);
-          step(n + 1, qop, sb, sa);
+        while (n < n1) {
+          set_bias();
+          f32x16_t sa[C::NKB], sb[C::NKB];
+          scores(n, qop, sa);
+          for (;;) {
+            const bool r0 = step(n, qop, sa, sb);
+            ++n;
+            if (r0 || n >= n1) break;
+            const bool r1 = step(n, qop, sb, sa);
+            ++n;
+            if (r1 || n >= n1) break;
+          }
         }
-        if (n < n1) step(n, qop, sa, sb);
       };
 
       const int npre = min(nfar, C::NSTAGE - 1);
       for (int n = 0; n < npre; ++n) issue(n);
       wait_vm<0>();
       __syncthreads();  // tiles 0 .. npre-1 in LDS
-      if (has_p2c) {
-        uint4 qop[NU];
-        q_plus(1, qop);   // keys left of the queries: bottom row
-        run(0, FL, qop);
-        q_plus(0, qop);   // keys right of the queries: top row
-        run(FL, nfar, qop);
-      } else {
-        run(0, nfar, qf);
-      }
+      const float a_left = has_c2p ? a_top : 0.f, a_right = has_c2p ? a_bot : 0.f;
+      uint4 qop[NU];
+      // keys left of the queries read the bottom qr row, keys right the top
+      q_scaled(has_p2c ? 1 : -1, qop);
+      run(0, FL, qop, a_left);
+      if (has_p2c) q_scaled(0, qop);
+      run(FL, nfar, qop, a_right);
     }
   }
 

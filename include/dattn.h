@@ -28,7 +28,14 @@
  *     synchronises with the host. A DATTN_OK return means the work was
  *     enqueued.
  *   - Element types (dtype): DATTN_F32, DATTN_F16, DATTN_BF16. q, k, v, qr,
- *     kr and out all use the same type. Accumulation is in fp32.
+ *     kr and out all use the same type. Accumulation is in fp32. For the
+ *     16-bit types the softmax weights are rounded to the element type
+ *     before the P.V product, and on key tiles beyond the table's two
+ *     saturation distances the forward forms the operand
+ *     (q_i + qr[edge row]) * scale * log2(e) in fp32 and rounds it once to
+ *     the element type (q_i * scale * log2(e) without P2C). With fp16 and a
+ *     caller scale above ~0.69 that product can leave fp16's range where
+ *     q_i + qr[row] alone would not; the default scales shrink it.
  *   - Head h of a token row occupies columns h*d .. h*d+d-1.
  *   - Row strides (ld_*) are in elements, must be >= H*d and a multiple of
  *     16 bytes; every array pointer must be 16-byte aligned. A fused QKV

@@ -4,8 +4,9 @@ oracle (oracle.backward.lse_rows).
 Bar, absolute: 1e-5 (fp32), 5e-3 (fp16), 1e-2 (bf16). lse is the log of the
 row sum of exponentials, so a change of every score by at most e moves it by
 at most e. The scores carry the products of inputs in the element type
-accumulated in fp32 and, on far tiles, the operand q_i + qr[row] rounded
-once (relative 2^-9 bf16, 2^-11 fp16). For the 16-bit types the row sum is
+accumulated in fp32 and, on far tiles, the operand
+(q_i + qr[row]) * scale * log2(e) rounded once (relative 2^-9 bf16, 2^-11
+fp16). For the 16-bit types the row sum is
 taken from the exponentials after they are rounded to the element type (the
 same P the P.V product reads), each term off by at most that relative
 amount, which moves the log of the sum by at most 2^-9 (bf16) or 2^-11
