@@ -219,8 +219,21 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int item, unsigned 
     }
     base = (int64_t)b * p.L;
     row_limit = p.L;
+    bool zero_tile = false;
     if (p.mask) {
       mrow = p.mask + (int64_t)b * p.L;
+      // A query tile with no valid position at or after its first row holds
+      // no valid query (its rows are zero): every wave reads those mask bytes
+      // and reaches the same answer, so such a tile (most of a heavily padded
+      // batch) skips the extent scan and its barriers.
+      int any = 0;
+      for (int j = qt * BM + lane; j < p.L; j += 64) any |= mrow[j];
+      zero_tile = !__any(any != 0);
+    }
+    if (zero_tile) {
+      ext = 0;
+      first_bad = 0;
+    } else if (p.mask) {
       if (tid == 0) { misc[0] = 0; misc[1] = p.L; }
       __syncthreads();
       int last = 0, firstz = p.L;
@@ -1224,10 +1237,15 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int item, unsigned 
       else phase1g(std::false_type{});
     }
 
-    // ---- phase 2 (16-bit types): far tiles through the LDS ring -----------
-    // Far tiles 0..FL-1 and FR..tm-1 are numbered n = 0, 1, ...; tile n lives
-    // in ring slot n % NSTAGE. Loads run three tiles ahead and are waited for
-    // two steps after they are issued; one barrier per tile publishes them.
+    // ---- phase 2 (16-bit types): far tiles through LDS rings ---------------
+    // Far tiles 0..FL-1 and FR..tm-1 are numbered n = 0, 1, ...; K tiles pass
+    // through a ring of 3 slots (tile n in slot n % 3) and V tiles through a
+    // ring of 5 (slot n % 5), filled by direct-to-LDS loads issued three
+    // tiles ahead and waited for two steps after they are issued; one
+    // barrier per tile publishes them.
+    // Two-stage pipeline: step n issues, in one block, the Q.K MFMAs of tile
+    // n+1 and the P.V MFMAs of tile n-1 between tile n's exponentials, so
+    // the matrix unit has work while the exponentials run.
     // On far tiles the P2C term is k_j . qr[row] with one saturated row per
     // side, so it joins the Q.K product, and the softmax scale joins it too:
     // the B operand is (q_i + qr[row]) * tau * log2(e) (formed in fp32,
@@ -1238,11 +1256,12 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int item, unsigned 
     const int nfar = FL + max(tm - FR, 0);
     if (nfar > 0) {
       const float tl2 = p.scale_log2;
-      // tile n in ring slot n % NSTAGE: its K tile, then its V tile
-      static_assert((C::NSTAGE & (C::NSTAGE - 1)) == 0, "ring slots: a power of two");
-      auto ring_slot = [](int n) { return (uint32_t)n & (C::NSTAGE - 1); };   // n >= 0
-      auto kslot = [&](int n) { return smem + ring_slot(n) * C::SLOT_BYTES; };
-      auto vslot = [&](int n) { return kslot(n) + C::KT_BYTES; };
+      constexpr int KS = 3, VS = 5;   // ring slots
+      static_assert((KS + VS) * C::KT_BYTES <= C::RING_BYTES, "rings exceed the ring region");
+      auto kslot_of = [](int n) { return (uint32_t)n % KS; };   // n >= 0
+      auto vslot_of = [](int n) { return (uint32_t)n % VS; };
+      auto kslot = [&](int n) { return smem + kslot_of(n) * C::KT_BYTES; };
+      auto vslot = [&](int n) { return smem + (KS + vslot_of(n)) * C::KT_BYTES; };
       // Tiles are issued in order n = 0, 1, ..., so their sources follow
       // running pointers: one tile apart, with a jump over the general
       // tiles [FL, FR) when the right-hand run starts.
@@ -1253,11 +1272,12 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int item, unsigned 
       const uint32_t wring = (uint32_t)__builtin_amdgcn_readfirstlane((int)(ring + 1024 * wave * DPW));
       auto issue = [&](int n) {
         if (__builtin_expect(n == FL, 0)) { kt_nx += kjump; vt_nx += vjump; }
-        const uint32_t slot = wring + ring_slot(n) * C::SLOT_BYTES;
+        const uint32_t ks = wring + kslot_of(n) * C::KT_BYTES;
+        const uint32_t vs = wring + (KS + vslot_of(n)) * C::KT_BYTES;
 #pragma unroll
-        for (int x = 0; x < DPW; ++x) dma16(slot + 1024 * x, kt_nx, kdo[x]);
+        for (int x = 0; x < DPW; ++x) dma16(ks + 1024 * x, kt_nx, kdo[x]);
 #pragma unroll
-        for (int x = 0; x < DPW; ++x) dma16(slot + C::KT_BYTES + 1024 * x, vt_nx, vdo[x]);
+        for (int x = 0; x < DPW; ++x) dma16(vs + 1024 * x, vt_nx, vdo[x]);
         kt_nx += kstep;
         vt_nx += vstep;
       };
@@ -1294,15 +1314,9 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int item, unsigned 
         for (int r = 0; r < 16; ++r) bias[r] = b;
       };
 
-      // Software-pipelined: the scores of tile n+1 are produced by MFMAs
-      // issued in the same block as tile n's exponentials.
-      // The two key blocks' MFMA chains are interleaved, so no MFMA waits
-      // for the result of the one issued just before it.
-      auto scores = [&](int n, const uint4 (&qop)[NU], f32x16_t (&s)[C::NKB]) {
-        const unsigned char* ks = kslot(n);
-        uint4 kf[C::NKB][NU];
-#pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb) k_operand(ks, kb, kf[kb]);
+      // Scores of tile n from K rows kf; the two key blocks' MFMA chains are
+      // interleaved, so no MFMA waits for the one issued just before it.
+      auto scores_from = [&](const uint4 (&kf)[C::NKB][NU], const uint4 (&qop)[NU], f32x16_t (&s)[C::NKB]) {
 #pragma unroll
         for (int kb = 0; kb < C::NKB; ++kb) s[kb] = bias;
 #pragma unroll
@@ -1310,6 +1324,23 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int item, unsigned 
 #pragma unroll
           for (int kb = 0; kb < C::NKB; ++kb)
             s[kb] = Ty<T>::mma(frag_at<T, NU>(kf[kb], c), frag_at<T, NU>(qop, c), s[kb]);
+      };
+      auto scores = [&](int n, const uint4 (&qop)[NU], f32x16_t (&s)[C::NKB]) {
+        const unsigned char* ks = kslot(n);
+        uint4 kf[C::NKB][NU];
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb) k_operand(ks, kb, kf[kb]);
+        scores_from(kf, qop, s);
+      };
+      // the same from global memory: the cold path of step n, whose K slot
+      // already receives tile n+3
+      auto scores_global = [&](int n, const uint4 (&qop)[NU], f32x16_t (&s)[C::NKB]) {
+        const int64_t j0 = (int64_t)(n < FL ? n : FR + (n - FL)) * BN;
+        uint4 kf[C::NKB][NU];
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb)
+          load_half_row<NU>(kf[kb], Kg + ((base + j0 + 32 * kb + li) * p.ld_k + hoff + lh * C::HALF) * ES);
+        scores_from(kf, qop, s);
       };
       // P = exp2(s - sub) rounded to the element type, into pf; returns
       // this lane's sum of the rounded P (sub only on the cold path)
@@ -1335,29 +1366,31 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int item, unsigned 
           }
         return (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
       };
-      // tile n: scores in s_cur; produces the scores of tile n+1 in s_nxt.
+      // Step n: scores of tile n in s_cur (read from K slot n % 3 before the
+      // barrier that ended step n-1, or before a barrier of their own),
+      // P of tile n-1 in pf_prev (its
+      // P.V is still due). Forms the scores of tile n+1 in s_nxt and P of
+      // tile n in pf_cur, and accumulates P.V of tile n-1.
       // The offset m_run is raised only when a tile's maximum exceeds it by
       // more than 8; the exponentials are taken against the current offset
       // and their row-half sum (at most 32 * 2^8 when no raise is due)
       // detects a due raise or an overflow. That rare case, and a lane with
-      // no offset yet, forms the tile's scores again from the ring, raises
-      // the offset, redoes the exponentials and moves the next tile's
-      // scores (formed with the old offset) to the new one.
-      // Returns true when it raised the offset: the bias block is then out of
-      // date, and so are the scores of tile n+1 formed here.
+      // no offset yet, forms the tile's scores again, raises the offset and
+      // redoes the exponentials. Returns true when it raised the offset: the
+      // bias block is then out of date, and so are the scores of tile n+1.
       auto step = [&](int n, const uint4 (&qop)[NU], f32x16_t (&s_cur)[C::NKB],
-                      f32x16_t (&s_nxt)[C::NKB]) -> bool {
-        const bool more = n + C::NSTAGE - 1 < nfar;
-        if (more) issue(n + C::NSTAGE - 1);   // into the slot of tile n-1
-        PFrag pf;
+                      f32x16_t (&s_nxt)[C::NKB], const PFrag& pf_prev, PFrag& pf_cur) -> bool {
+        const bool more = n + 3 < nfar;
+        if (more) issue(n + 3);   // K slot of tile n, V slot of tile n-2
         // unconditional, so the MFMAs share a block with the exponentials;
         // past the last tile of a run they read a slot whose result is not
         // used
         scores(n + 1, qop, s_nxt);
-        float ps = exps(s_cur, pf, std::false_type{}, 0.f);
+        pv_acc(pf_prev, s_cur, vop_slot(vslot(n + VS - 1)));   // tile n-1
+        float ps = exps(s_cur, pf_cur, std::false_type{}, 0.f);
         bool raised = false;
         if (__builtin_expect(__any(!(ps <= 32.f * 256.f) || m_run == NEG_INF), 0)) {
-          scores(n, qop, s_cur);
+          scores_global(n, qop, s_cur);
           float mx4[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
 #pragma unroll
           for (int kb = 0; kb < C::NKB; ++kb)
@@ -1373,26 +1406,33 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int item, unsigned 
           const float m_eff = m_run == NEG_INF ? 0.f : m_run;
           const bool raise = m_run == NEG_INF || mxf > 8.f;
           const float m_new = raise ? m_eff + mxf : m_run;
-          // m_run == -inf: nothing accumulated yet, alpha = exp2(-inf) = 0
+          // m_run == -inf: nothing accumulated yet, alpha = exp2(-inf) = 0;
+          // o_acc already holds tile n-1's P.V, taken at the old offset
           const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
           l_part *= alpha;
 #pragma unroll
           for (int x = 0; x < C::NDB; ++x) o_acc[x] *= alpha;
           const float delta = m_new - m_eff;   // 0 without a raise
           m_run = m_new;
-          ps = exps(s_cur, pf, std::true_type{}, delta);
+          ps = exps(s_cur, pf_cur, std::true_type{}, delta);
           raised = __any(raise);
         }
         l_part += ps;
-        pv_acc(pf, s_cur, vop_slot(vslot(n)));
         // tile n+2, read from the next step on, has landed once at most the
         // loads of tile n+3 are in flight; after the barrier it is visible
-        // and the slot of tile n is free
+        // and the K slot of tile n+1 and the V slot of tile n-1 are free
         if (more) wait_vm<2 * DPW>();
         else wait_vm<0>();
         __syncthreads();
         return raised;
       };
+      // The P.V of tile n-1 is due at step n. Before the first far tile it
+      // is a zero P against a zero-filled V slot (the slot of tile -1).
+      PFrag pfa, pfb;   // pfb: the pending P
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) pfb[kb][c2] = __builtin_bit_cast(typename Ty<T>::frag, make_uint4(0, 0, 0, 0));
       // tiles n0 .. n1-1 with B operand qop and C2P constant a_off. The bias
       // block is constant inside the inner loop; a raise of the offset
       // leaves it, and the outer loop forms the next tile's scores again
@@ -1404,21 +1444,38 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int item, unsigned 
           set_bias();
           f32x16_t sa[C::NKB], sb[C::NKB];
           scores(n, qop, sa);
+          // step n loads tile n+3 into the K slot just read: every wave's
+          // reads of it come first
+          __syncthreads();
           for (;;) {
-            const bool r0 = step(n, qop, sa, sb);
+            const bool r0 = step(n, qop, sa, sb, pfb, pfa);
             ++n;
-            if (r0 || n >= n1) break;
-            const bool r1 = step(n, qop, sb, sa);
+            if (r0 || n >= n1) {
+#pragma unroll
+              for (int kb = 0; kb < C::NKB; ++kb) {
+                pfb[kb][0] = pfa[kb][0];
+                pfb[kb][1] = pfa[kb][1];
+              }
+              break;
+            }
+            const bool r1 = step(n, qop, sb, sa, pfa, pfb);
             ++n;
             if (r1 || n >= n1) break;
           }
         }
       };
 
-      const int npre = min(nfar, C::NSTAGE - 1);
+      const int npre = min(nfar, 3);
       for (int n = 0; n < npre; ++n) issue(n);
+      {
+        // zero V slot VS-1, the slot of tile -1 (written by tile VS-1, issued
+        // after the first step's barrier)
+        unsigned char* z = smem + (KS + VS - 1) * C::KT_BYTES;
+        for (int x = tid; x < C::KT_BYTES / 16; x += NT)
+          *reinterpret_cast<uint4*>(z + 16 * x) = make_uint4(0, 0, 0, 0);
+      }
       wait_vm<0>();
-      __syncthreads();  // tiles 0 .. npre-1 in LDS
+      __syncthreads();  // tiles 0 .. npre-1 in LDS, V slot of tile -1 zero
       const float a_left = has_c2p ? a_top : 0.f, a_right = has_c2p ? a_bot : 0.f;
       uint4 qop[NU];
       // keys left of the queries read the bottom qr row, keys right the top
@@ -1426,6 +1483,9 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int item, unsigned 
       run(0, FL, qop, a_left);
       if (has_p2c) q_scaled(0, qop);
       run(FL, nfar, qop, a_right);
+      // the last tile's P.V
+      f32x16_t unused[C::NKB];
+      pv_acc(pfb, unused, vop_slot(vslot(nfar - 1)));
     }
   }
 
