@@ -1282,21 +1282,13 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int item, unsigned 
         vt_nx += vstep;
       };
       // (q_i + qr[row]) tau log2(e) (which: 0 top row, 1 bottom row, -1 no
-      // row) in this lane's layout. q_i is read again from global memory (a
-      // cache hit) rather than kept live through the far loop.
+      // row) in this lane's layout
       auto q_scaled = [&](int which, uint4 (&dst)[NU]) {
-        uint4 rf[NU], qg[NU];
-        const int qi = i0w + li;
-        if (qi < ext) {
-          load_half_row<NU>(qg, Qg + ((base + qi) * p.ld_q + hoff + lh * C::HALF) * ES);
-        } else {
-#pragma unroll
-          for (int x = 0; x < NU; ++x) qg[x] = make_uint4(0, 0, 0, 0);
-        }
+        uint4 rf[NU];
         if (which >= 0) lds_half_row<NU>(rf, Rrows + which * D * ES + lh * C::HALF * ES);
 #pragma unroll
         for (int x = 0; x < NU; ++x) {
-          const auto a = __builtin_bit_cast(typename Ty<T>::frag, qg[x]);
+          const auto a = __builtin_bit_cast(typename Ty<T>::frag, qf[x]);
           const auto b = __builtin_bit_cast(typename Ty<T>::frag, rf[x]);
           f32x8_t v;
 #pragma unroll
