@@ -302,3 +302,45 @@ def test_short_packed_tile_dispatch(dtype, d):
         err = float(np.abs(got - want).max())
         print(f"short packed {dtype} d={d} bound={bound}: {err:.2e}", file=sys.stderr, flush=True)
         assert err <= H.TOL[dtype], (bound, err)
+
+
+# Keys whose scores jump by more than 8 (base-2 units) from one far tile to a
+# later one make the far loop raise its softmax offset in the middle of a run
+# (left of the queries and right of them): the cold path forms the tile's
+# scores again from global memory, rescales the accumulators that already
+# hold the previous tile's P.V, and the loop restarts with a new bias block.
+# Spike keys carry q.k of 40 to 490 against queries along one axis, at least
+# 90 apart (more than 9 base-2 units at the default scale), so the largest
+# spike dominates every row and no two keys compete: the rounding of the far
+# tiles' scaled operand then stays well inside the bar. In key order the
+# spikes rise and fall, so runs see raises and tiles that need none.
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("packed", [False, True])
+def test_far_offset_raises_mid_run(dtype, packed):
+    L, Hh, d = 2048, 2, 64
+    w = workloads.make_workload("raise", dtype=dtype, B=1, L=L, H=Hh, d=d, position_buckets=256,
+                                max_relative_positions=512, seed=41, packed=packed, with_mask=False)
+    rng = np.random.default_rng(42)
+    q = 0.1 * rng.standard_normal(w.q.shape)
+    k = 0.1 * rng.standard_normal(w.k.shape)
+    for h in range(Hh):
+        q[..., h * d] += 2.0                                    # every query along axis 0
+    spikes = {90: 65.0, 600: 20.0, 1000: 155.0, 1400: 110.0, 1830: 245.0, 1990: 200.0}
+    for pos, c in spikes.items():
+        for h in range(Hh):
+            k[..., pos, h * d] += c
+    w.q = workloads.round_to(q, dtype)
+    w.k = workloads.round_to(k, dtype)
+    w.qr = workloads.round_to(0.05 * rng.standard_normal(w.qr.shape), dtype)
+    w.kr = workloads.round_to(0.05 * rng.standard_normal(w.kr.shape), dtype)
+    if packed:
+        got = H.host(H.run_varlen(w))
+        want = H.oracle_varlen(w)
+        err = float(np.abs(got - want).max())
+    else:
+        got = H.host(H.run_padded(w))
+        want = H.oracle_padded(w)
+        err = float(np.abs(got - want).max())
+    _say(f"far offset raises {dtype} packed={packed}: max abs err {err:.3e}")
+    assert np.all(np.isfinite(got))
+    assert err <= H.TOL[dtype], err
