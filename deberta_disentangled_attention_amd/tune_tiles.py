@@ -25,7 +25,7 @@ import sys
 from . import build as B
 
 ROOT = os.path.dirname(B.PKG_DIR)
-OUT_DIR = os.path.join(B.PKG_DIR, "_build", "tiles")
+OUT_DIR = os.path.join(B.PKG_DIR, "tune_bin")
 CANDIDATES = {
     "nw2": ["-DDATTN_NW_D32=2", "-DDATTN_NW_D64=2", "-DDATTN_NW_D128=4"],
     "nw4": ["-DDATTN_NW_D32=4", "-DDATTN_NW_D64=4", "-DDATTN_NW_D128=4"],
