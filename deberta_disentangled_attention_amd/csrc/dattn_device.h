@@ -141,6 +141,19 @@ __device__ __forceinline__ void lds_half_row(uint4 (&u)[NU], const unsigned char
 
 __device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32); }
 
+// wave-wide integer minimum / maximum; the result is wave-uniform (held
+// in a scalar register)
+__device__ __forceinline__ int wave_min_i(int x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = min(x, __shfl_xor(x, o));
+  return __builtin_amdgcn_readfirstlane(x);
+}
+__device__ __forceinline__ int wave_max_i(int x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = max(x, __shfl_xor(x, o));
+  return __builtin_amdgcn_readfirstlane(x);
+}
+
 // Direct-to-LDS load (global_load_lds_dwordx4): lane i's 16 bytes at
 // gbase + voff are written to LDS byte address lds + 16 i. The data bypasses
 // the registers; completion is tracked by this wave's vmcnt. Inline assembly

@@ -122,7 +122,8 @@ struct Cfg {
   static constexpr int OFF_R = OFF_C + C_BYTES;
   static constexpr int OFF_TW = OFF_R + R_BYTES;
   static constexpr int OFF_MISC = OFF_TW + TW_BYTES;
-  static constexpr int LDS_BYTES = OFF_MISC + 64;
+  static constexpr int MISC_INTS = 8 + 4 * NW;       // scalars, then two rounds of per-wave pairs
+  static constexpr int LDS_BYTES = OFF_MISC + 4 * MISC_INTS;
   // two workgroups per CU when they fit in its 160 KB of LDS
   static constexpr int WG_PER_CU = LDS_BYTES <= 80 * 1024 ? 2 : 1;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one CU exceeded");
@@ -219,34 +220,59 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int item, unsigned 
     }
     base = (int64_t)b * p.L;
     row_limit = p.L;
-    bool zero_tile = false;
     if (p.mask) {
+      // Every wave scans the whole mask row and reduces it itself (no
+      // barrier): ext = one past the last valid position, first_bad = the
+      // first padded one. A query tile with no valid query at or after its
+      // first row (most tiles of a heavily padded batch) then has
+      // qt * BM >= ext and leaves below.
       mrow = p.mask + (int64_t)b * p.L;
-      // A query tile with no valid position at or after its first row holds
-      // no valid query (its rows are zero): every wave reads those mask bytes
-      // and reaches the same answer, so such a tile (most of a heavily padded
-      // batch) skips the extent scan and its barriers.
-      int any = 0;
-      for (int j = qt * BM + lane; j < p.L; j += 64) any |= mrow[j];
-      zero_tile = !__any(any != 0);
-    }
-    if (zero_tile) {
-      ext = 0;
-      first_bad = 0;
-    } else if (p.mask) {
-      if (tid == 0) { misc[0] = 0; misc[1] = p.L; }
-      __syncthreads();
       int last = 0, firstz = p.L;
-      for (int j = tid; j < p.L; j += NT) {
-        if (mrow[j]) last = j + 1;
-        else if (j < firstz) firstz = j;
+      // loads in batches of 8 per lane, so that a batch costs one round trip
+      constexpr int MB = 8;
+      if ((p.L & 3) == 0 && (reinterpret_cast<uintptr_t>(mrow) & 3) == 0) {
+        const uint32_t* mw = reinterpret_cast<const uint32_t*>(mrow);
+        const int nw = p.L >> 2;
+        for (int w0 = 0; w0 < nw; w0 += 64 * MB) {
+          uint32_t m4[MB];
+#pragma unroll
+          for (int k = 0; k < MB; ++k) {
+            const int w = w0 + lane + 64 * k;
+            m4[k] = mw[min(w, nw - 1)];   // unconditional: the loads issue together
+          }
+#pragma unroll
+          for (int k = 0; k < MB; ++k) {
+            const int w = w0 + lane + 64 * k;
+            if (w < nw) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int j = 4 * w + e;
+                if ((m4[k] >> (8 * e)) & 0xffu) last = j + 1;
+                else firstz = min(firstz, j);
+              }
+            }
+          }
+        }
+      } else {
+        for (int j0 = 0; j0 < p.L; j0 += 64 * MB) {
+          uint8_t m1[MB];
+#pragma unroll
+          for (int k = 0; k < MB; ++k) {
+            const int j = j0 + lane + 64 * k;
+            m1[k] = mrow[min(j, p.L - 1)];
+          }
+#pragma unroll
+          for (int k = 0; k < MB; ++k) {
+            const int j = j0 + lane + 64 * k;
+            if (j < p.L) {
+              if (m1[k]) last = j + 1;
+              else firstz = min(firstz, j);
+            }
+          }
+        }
       }
-      if (last) atomicMax(&misc[0], last);
-      if (firstz < p.L) atomicMin(&misc[1], firstz);
-      __syncthreads();
-      ext = misc[0];
-      first_bad = misc[1];
-      __syncthreads();
+      ext = wave_max_i(last);
+      first_bad = wave_min_i(firstz);
     } else {
       ext = p.L;
       first_bad = p.L;
@@ -332,68 +358,8 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int item, unsigned 
       return row_off(r);
     }
   };
-  if (has_c2p || has_p2c) {
-    // The table is non-decreasing, so both thresholds (the first index that
-    // holds its last value, the first that leaves its first value) are found
-    // in two rounds: NT samples spaced `step` apart (the last one at n-1)
-    // bracket them, then one thread per bracket entry settles each. The
-    // window staged in LDS is the union of the two brackets and everything
-    // between them: its end entries are saturated, so clamping an index
-    // into it reproduces the table beyond the thresholds.
-    const int32_t* tb = p.rel_idx;
-    const int step = tbl_n > 1 ? (tbl_n - 2) / (NT - 1) + 1 : 1;
-    if (tid == 0) { misc[2] = NT; misc[3] = NT; misc[4] = tbl_n; misc[5] = tbl_n; }
-    row_hi = tb[tbl_n - 1];
-    row_lo = tb[0];
-    const int xs = min(tid * step, tbl_n - 1);
-    const int vs = tb[xs];
-    __syncthreads();
-    if (vs == row_hi) atomicMin(&misc[2], tid);
-    if (vs != row_lo) atomicMin(&misc[3], tid);
-    __syncthreads();
-    const int t_top = misc[2], t_bot = misc[3];   // t_top <= NT-1: the last sample is n-1
-    // brackets: first_top in (lo_top, hi_top], first_above_bot in (lo_bot, hi_bot]
-    const int hi_top = min(t_top * step, tbl_n - 1);
-    const int lo_top = t_top > 0 ? min((t_top - 1) * step, tbl_n - 1) : -1;
-    const bool flat = t_bot >= NT;                  // every entry equals the first
-    const int hi_bot = flat ? tbl_n : min(t_bot * step, tbl_n - 1);
-    const int lo_bot = flat ? tbl_n - 1 : (t_bot > 0 ? min((t_bot - 1) * step, tbl_n - 1) : -1);
-    // half of the threads search each bracket (at most `step` entries)
-    if (tid < NT / 2) {
-      for (int k = tid; k < step; k += NT / 2) {
-        const int x = lo_top + 1 + k;
-        if (x < hi_top && tb[x] == row_hi) atomicMin(&misc[4], x);
-      }
-    } else if (!flat) {
-      for (int k = tid - NT / 2; k < step; k += NT / 2) {
-        const int x = lo_bot + 1 + k;
-        if (x < hi_bot && tb[x] != row_lo) atomicMin(&misc[5], x);
-      }
-    }
-    // window: table entries lo_bot .. hi_top (clamped into the table)
-    const int w0 = max(lo_bot, 0), w1 = max(hi_top, w0);
-    tw0 = w0 - (R - 1);
-    tw_n = w1 - w0 + 1;
-    tw_ok = !flat && tw_n <= C::TW;
-    if (tw_ok)
-      for (int x = tid; x < tw_n; x += NT) Tw[x] = row_off(tb[w0 + x]);
-    __syncthreads();
-    const int first_top = min(misc[4], hi_top);
-    const int first_above_bot = flat ? tbl_n : min(misc[5], hi_bot);
-    sat_top = first_top - (R - 1);
-    sat_bot = first_above_bot - 1 - (R - 1);
-    // stage the two saturation rows of qr and kr (this head) in LDS
-    constexpr int RU = D * ES / 16;
-    for (int x = tid; x < 4 * RU; x += NT) {
-      const int which = x / RU, u = x - which * RU;
-      const unsigned char* tab = (which < 2) ? QRg : KRg;
-      const int row = clamp_row((which & 1) ? row_lo : row_hi);
-      *reinterpret_cast<uint4*>(Rrows + which * D * ES + 16 * u) =
-          ld16(tab + ((int64_t)row * p.ld_rel + hoff) * ES + 16 * u);
-    }
-  }
-
-  // this lane's query row, half of the head dim (B operand of every product)
+  // this lane's query row, half of the head dim (B operand of every
+  // product); issued first so that its latency overlaps the table's
   uint4 qf[NU];
   {
     const int qi = i0w + li;
@@ -405,7 +371,106 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int item, unsigned 
     }
   }
 
-  __syncthreads();  // saturation rows and table window staged
+  if (has_c2p || has_p2c) {
+    // The table is non-decreasing, so both thresholds (the first index that
+    // holds its last value, the first that leaves its first value) are
+    // bracketed by NT samples spaced `step` apart (the last one at n-1) and
+    // then settled exactly by the entries inside the two brackets. The
+    // window staged in LDS is the union of the two brackets and everything
+    // between them: its end entries are saturated, so clamping an index
+    // into it reproduces the table beyond the thresholds. A table that fits
+    // the window buffer is read whole together with the samples (one round
+    // of loads); a longer one is read in a second round, the window only.
+    // Cross-wave results go through per-wave LDS slots, one barrier each.
+    const int32_t* tb = p.rel_idx;
+    const int step = tbl_n > 1 ? (tbl_n - 2) / (NT - 1) + 1 : 1;
+    constexpr int TPT = C::TW / NT;   // entries per thread of a whole table
+    const bool whole = tbl_n <= C::TW;
+    row_hi = tb[tbl_n - 1];
+    row_lo = tb[0];
+    const int vs = tb[min(tid * step, tbl_n - 1)];
+    int ent[TPT];
+    const int nk = (tbl_n + NT - 1) / NT;   // chunks of NT entries a whole table has
+    if (whole) {
+#pragma unroll
+      for (int k = 0; k < TPT; ++k) {
+        const int x = tid + k * NT;
+        ent[k] = k < nk ? tb[min(x, tbl_n - 1)] : 0;
+      }
+    }
+    // minimum over the workgroup of a wave-reduced pair, through slots at o
+    auto block_min2 = [&](int a, int b, int o) -> int2 {
+      if (lane == 0) { misc[o + 2 * wave] = a; misc[o + 2 * wave + 1] = b; }
+      __syncthreads();
+      int2 r = make_int2(misc[o], misc[o + 1]);
+#pragma unroll
+      for (int w = 1; w < NW; ++w) {
+        r.x = min(r.x, misc[o + 2 * w]);
+        r.y = min(r.y, misc[o + 2 * w + 1]);
+      }
+      return make_int2(__builtin_amdgcn_readfirstlane(r.x), __builtin_amdgcn_readfirstlane(r.y));
+    };
+    // first sample holding the last value (exists: the last sample is n-1)
+    // and first sample leaving the first value (NT: none, a flat table)
+    const int2 tt = block_min2(wave_min_i(vs == row_hi ? tid : NT), wave_min_i(vs != row_lo ? tid : NT), 8);
+    const int t_top = tt.x, t_bot = tt.y;
+    // brackets: first_top in (lo_top, hi_top], first_above_bot in (lo_bot, hi_bot]
+    const int hi_top = min(t_top * step, tbl_n - 1);
+    const int lo_top = t_top > 0 ? min((t_top - 1) * step, tbl_n - 1) : -1;
+    const bool flat = t_bot >= NT;                  // every entry equals the first
+    const int hi_bot = flat ? tbl_n : min(t_bot * step, tbl_n - 1);
+    const int lo_bot = flat ? tbl_n - 1 : (t_bot > 0 ? min((t_bot - 1) * step, tbl_n - 1) : -1);
+    // window: table entries lo_bot .. hi_top (clamped into the table); it
+    // contains both brackets
+    const int w0 = max(lo_bot, 0), w1 = max(hi_top, w0);
+    tw0 = w0 - (R - 1);
+    tw_n = w1 - w0 + 1;
+    tw_ok = !flat && tw_n <= C::TW;
+    int ftop = tbl_n, fbot = tbl_n;
+    auto settle = [&](int x, int v) {
+      if (x > lo_top && x < hi_top && v == row_hi) ftop = min(ftop, x);
+      if (!flat && x > lo_bot && x < hi_bot && v != row_lo) fbot = min(fbot, x);
+    };
+    if (whole) {
+#pragma unroll
+      for (int k = 0; k < TPT; ++k) {
+        const int x = tid + k * NT;
+        if (k < nk && x < tbl_n) {
+          settle(x, ent[k]);
+          if (tw_ok && x >= w0 && x <= w1) Tw[x - w0] = row_off(ent[k]);
+        }
+      }
+    } else if (tw_ok) {
+      for (int x = tid; x < tw_n; x += NT) {
+        const int v = tb[w0 + x];
+        Tw[x] = row_off(v);
+        settle(w0 + x, v);
+      }
+    } else {
+      // window too long to stage: the two brackets only (at most `step`
+      // entries each)
+      for (int k = tid; k < step; k += NT) {
+        const int xt = lo_top + 1 + k, xb = lo_bot + 1 + k;
+        if (xt < hi_top) settle(xt, tb[xt]);
+        if (!flat && xb < hi_bot) settle(xb, tb[xb]);
+      }
+    }
+    // stage the two saturation rows of qr and kr (this head) in LDS
+    constexpr int RU = D * ES / 16;
+    for (int x = tid; x < 4 * RU; x += NT) {
+      const int which = x / RU, u = x - which * RU;
+      const unsigned char* tab = (which < 2) ? QRg : KRg;
+      const int row = clamp_row((which & 1) ? row_lo : row_hi);
+      *reinterpret_cast<uint4*>(Rrows + which * D * ES + 16 * u) =
+          ld16(tab + ((int64_t)row * p.ld_rel + hoff) * ES + 16 * u);
+    }
+    // (this barrier also publishes the window and the saturation rows)
+    const int2 ff = block_min2(wave_min_i(ftop), wave_min_i(fbot), 8 + 2 * NW);
+    const int first_top = min(ff.x, hi_top);
+    const int first_above_bot = flat ? tbl_n : min(ff.y, hi_bot);
+    sat_top = first_top - (R - 1);
+    sat_bot = first_above_bot - 1 - (R - 1);
+  }
 
   // a_i at both saturation ends: kr[row] . q_i with every A row equal
   float a_top = 0.f, a_bot = 0.f;
