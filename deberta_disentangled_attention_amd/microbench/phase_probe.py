@@ -1,8 +1,9 @@
-"""Where a forward workgroup spends its time: cycles per wave in the general
-(band) tiles and in the far tiles, and inside the general tiles the split
-between the tile start (load wait and barrier), the score products (C2C,
-the band products E and F and their diagonal gathers) and the softmax with
-P.V.
+"""Where a forward workgroup spends its time: cycles per wave in the
+prologue (from the work item's start to its first tile: mask or sequence
+search, Q row, relative-table thresholds and window), in the general (band)
+tiles and in the far tiles, and inside the general tiles the split between
+the tile start (load wait and barrier), the score products (C2C, the band
+products E and F and their diagonal gathers) and the softmax with P.V.
 
 It builds a separate library from a copy of the kernel sources with
 s_memtime reads inserted at the phase boundaries; that library's *_lse
@@ -32,7 +33,7 @@ ROOT = os.path.dirname(B.PKG_DIR)
 
 COUNTERS = ["general tiles, all", "far tiles, all", "general tiles (count)", "far steps (count)",
             "general: start (wait, barrier, loads issue)", "general: score products",
-            "general: softmax + P.V"]
+            "general: softmax + P.V", "prologue"]
 
 
 def _sub(text: str, anchor: str, new: str) -> str:
@@ -43,11 +44,12 @@ def _sub(text: str, anchor: str, new: str) -> str:
 
 def instrument(src: str) -> str:
     stamp = "__builtin_amdgcn_s_memtime()"
+    src = _sub(src, "  constexpr int NT = C::NT;\n", f"  constexpr int NT = C::NT;\n  const uint64_t pe_ = {stamp};\n")
     src = _sub(src, "  const int key_end = min(ext, first_bad);  // keys below this need no mask test",
                "  const int key_end = min(ext, first_bad);  // keys below this need no mask test\n"
-               "  float pc_[7] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};\n  uint64_t pg0_ = 0, pt_ = 0, pf0_ = 0;")
+               "  float pc_[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};\n  uint64_t pg0_ = 0, pt_ = 0, pf0_ = 0;")
     src = _sub(src, "    if (first_general >= 0) {\n      if (tw_ok) phase1g(std::true_type{});",
-               f"    pg0_ = {stamp};\n    if (first_general >= 0) {{\n      if (tw_ok) phase1g(std::true_type{{}});")
+               f"    pg0_ = {stamp};\n    pc_[7] = (float)(pg0_ - pe_);\n    if (first_general >= 0) {{\n      if (tw_ok) phase1g(std::true_type{{}});")
     src = _sub(src, "    const int nfar = FL + max(tm - FR, 0);\n    if (nfar > 0) {\n      const float tl2",
                f"    pf0_ = {stamp};\n    pc_[0] += (float)(pf0_ - pg0_);\n"
                "    const int nfar = FL + max(tm - FR, 0);\n    pc_[3] += (float)nfar;\n"
@@ -68,7 +70,7 @@ def instrument(src: str) -> str:
                "        pc_[2] += 1.f;\n")
     src = _sub(src, "      p.lse[(base + qi) * p.H + head] = row_ok ? (m_run + log2f(l_tot)) * 0.6931471805599453f : NEG_INF;",
                "      { const int kk_ = li & 7; float v_ = 0.f;\n"
-               "#pragma unroll\n        for (int z_ = 0; z_ < 7; ++z_) if (kk_ == z_) v_ = pc_[z_];\n"
+               "#pragma unroll\n        for (int z_ = 0; z_ < 8; ++z_) if (kk_ == z_) v_ = pc_[z_];\n"
                "        p.lse[(base + qi) * p.H + head] = v_; }")
     return src
 
@@ -135,7 +137,7 @@ def run(workloads) -> None:
         L = lse.float().cpu().numpy().reshape(-1, w.H)
         # counter c of a wave sits in its rows 8g + c; waves with no general
         # tile (count 0) are left out of the per-tile averages
-        c = [L[i::8].reshape(-1) for i in range(7)]
+        c = [L[i::8].reshape(-1) for i in range(8)]
         n = np.minimum.reduce([len(x) for x in c])
         c = [x[:n] for x in c]
         # waves of query tiles with no valid query return before the
@@ -145,10 +147,11 @@ def run(workloads) -> None:
         live = c[2] > 0
         per_g = lambda x: float(np.mean(x[live] / c[2][live])) if live.any() else 0.0
         vals = [np.mean(c[0]), np.mean(c[1]), np.mean(c[2]), np.mean(c[3]), per_g(c[4]), per_g(c[5]),
-                per_g(c[6])]
+                per_g(c[6]), np.mean(c[7])]
         print(f"| {name} | " + " | ".join(f"{x:.0f}" if i not in (2, 3) else f"{x:.1f}"
                                             for i, x in enumerate(vals)) + " |", flush=True)
-    print("\nTotals are cycles per wave (s_memtime); the three general-tile parts are cycles per general tile.")
+    print("\nTotals and the prologue are cycles per wave (s_memtime); the three general-tile parts are"
+          " cycles per general tile.")
 
 
 if __name__ == "__main__":
