@@ -849,6 +849,59 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int item, unsigned 
     softmax_pv_mid(s, a_off, vop, [] {}, nullptr);
   };
 
+  // Online softmax and P.V of one 32-key half of a tile (16-bit types, 16
+  // scores per lane): the same offset rule as softmax_p (raise only past a
+  // margin of 8, detected from the half's maximum); P rounded to the element
+  // type, its row sum taken from the rounded values.
+  auto softmax_pv_half = [&](f32x16_t& sv, int kb, float a_off, auto vop) {
+    if constexpr (ES == 2) {
+      const float tl2 = p.scale_log2;
+      const float off = a_off * tl2;
+      float mx4[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
+#pragma unroll
+      for (int r = 0; r < 16; r += 4) {
+        mx4[0] = fmaxf(mx4[0], sv[r]);
+        mx4[1] = fmaxf(mx4[1], sv[r + 1]);
+        mx4[2] = fmaxf(mx4[2], sv[r + 2]);
+        mx4[3] = fmaxf(mx4[3], sv[r + 3]);
+      }
+      const float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
+      const float mt_half = (mx == NEG_INF) ? NEG_INF : fmaf(mx, tl2, off);
+      if (__builtin_expect(__any(mt_half > m_run + 8.f), 0)) {
+        const float mxf = fmaxf(mx, wave_xor32(mx));
+        const float mt = (mxf == NEG_INF) ? NEG_INF : fmaf(mxf, tl2, off);
+        const bool raise = mt > m_run + 8.f;
+        const float m_new = raise ? mt : m_run;
+        // m_run == -inf: nothing accumulated yet, alpha = exp2(-inf) = 0
+        const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+        l_part *= alpha;
+#pragma unroll
+        for (int x = 0; x < C::NDB; ++x) o_acc[x] *= alpha;
+        m_run = m_new;
+      }
+      const float bias = off - (m_run == NEG_INF ? 0.f : m_run);
+      typename Ty<T>::frag pf[2];
+      float ps4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        f32x8_t e8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) e8[e] = __builtin_amdgcn_exp2f(fmaf(sv[8 * c2 + e], tl2, bias));
+        pf[c2] = Ty<T>::cvt8(e8);
+        const uint4 w = __builtin_bit_cast(uint4, pf[c2]);
+        ps4[0] = Ty<T>::sum2(w.x, ps4[0]);
+        ps4[1] = Ty<T>::sum2(w.y, ps4[1]);
+        ps4[2] = Ty<T>::sum2(w.z, ps4[2]);
+        ps4[3] = Ty<T>::sum2(w.w, ps4[3]);
+      }
+      l_part += (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) o_acc[db] = Ty<T>::mma(vop(kb, c2, db), pf[c2], o_acc[db]);
+    }
+  };
+
   // ---- tile classes -------------------------------------------------------
   // Tiles before tm need no mask test. A tile is "far" when every pair of it
   // lies beyond the saturation distances of each enabled term, on the side
@@ -1144,15 +1197,20 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int item, unsigned 
       // Table rows of the band operands: for half kb of tile t, E block ub
       // covers the distances u = umin + 32 ub + 0..31 and F block vb the
       // distances v = vmin + 32 vb + 0..31; lane li fetches row li of a block.
-      // The second half of a tile shares one block with the first: its E
-      // block 1 is the first half's E block 0 (same rows and queries, so the
-      // product is kept, not recomputed) and its F block 0 uses the first
-      // half's F block-1 rows. Two register blocks hold the rows in turn,
-      // each refetched as soon as a product has read it.
+      // Adjacent 32-key halves (the two halves of a tile, or the last half
+      // of a tile and the first of the next tile when that is the adjacent
+      // one) share blocks: a half's E block 1 is the E block 0 of the half
+      // before it (same rows and queries, so the product is kept in
+      // registers, not recomputed) and its F block 0 uses that half's F
+      // block-1 rows. Three register blocks hold the rows: rE the E block 0,
+      // rF[kb] and rF[kb ^ 1] the F blocks 0 and 1 of half kb (so the F
+      // block-1 rows of one half are already in place as the next half's
+      // block 0). Each half fetches the next half's rows as soon as its own
+      // products have read the buffers, a whole half ahead of their use.
       const unsigned char* krb = KRg + hoff * ES;   // this head's columns
       const unsigned char* qrb = QRg + hoff * ES;
       const uint32_t lhb = (uint32_t)(lh * C::HALF * ES);
-      uint4 rw[2][NU];
+      uint4 rE[NU], rF[2][NU];
       auto load_e = [&](int t, int kb, int ub, uint4 (&dst)[NU]) {
         const int umin = i0w - (t * BN + 32 * kb + 31);
         load_half_row<NU>(dst, krb + (rel_off(umin + 32 * ub + li, twok) + lhb));
@@ -1160,11 +1218,6 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int item, unsigned 
       auto load_f = [&](int t, int kb, int vb, uint4 (&dst)[NU]) {
         const int vmin = (t * BN + 32 * kb) - (i0w + 31);
         load_half_row<NU>(dst, qrb + (rel_off(vmin + 32 * vb + li, twok) + lhb));
-      };
-      // the rows the first half of tile t starts with (modes m)
-      auto load_first = [&](int t, const Modes& m) {
-        if (m.c2p == TERM_BAND) { load_e(t, 0, 0, rw[0]); load_e(t, 0, 1, rw[1]); }
-        else if (m.p2c == TERM_BAND) { load_f(t, 0, 0, rw[0]); load_f(t, 0, 1, rw[1]); }
       };
       // E[u][i] (two 32-distance blocks) into the scratch, then added along
       // the diagonal; likewise F[j][v]. The scratch is rewritten only after
@@ -1177,11 +1230,12 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int item, unsigned 
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[r] += e_rd[(27 - rr_of(r)) * 32];
       };
-      auto add_f = [&](const f32x16_t& f0, const f32x16_t& f1, f32x16_t& acc) {
+      // F block vb into the scratch; then its diagonal added
+      auto put_f = [&](const f32x16_t& f, int vb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) scr[(rr_of(r) + 4 * lh) * 64 + li] = f0[r];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) scr[(rr_of(r) + 4 * lh) * 64 + 32 + li] = f1[r];
+        for (int r = 0; r < 16; ++r) scr[(rr_of(r) + 4 * lh) * 64 + 32 * vb + li] = f[r];
+      };
+      auto sum_f = [&](f32x16_t& acc) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[r] += f_rd[rr_of(r) * 65];
       };
@@ -1189,8 +1243,12 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int item, unsigned 
       int t = first_general;
       int par = 0;   // slot of tile t
       issue_tile(t, ring);
-      Modes m = wave_modes(t);
-      load_first(t, uniform(m));
+      Modes m = uniform(wave_modes(t));
+      // rows of the first half
+      if (m.c2p == TERM_BAND) load_e(t, 0, 0, rE);
+      if (m.p2c == TERM_BAND) { load_f(t, 0, 0, rF[0]); load_f(t, 0, 1, rF[1]); }
+      f32x16_t e_keep = f32x16_t{};   // E block 1 of the coming half, valid when ek
+      bool ek = false;
       while (t >= 0) {
         const int tn = next_general(t);
         const int j0 = t * BN;
@@ -1227,8 +1285,6 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int item, unsigned 
 #pragma unroll
           for (int g = 0; g < BN / 16; ++g) c_group(ks, g, m.which, cjw);
         }
-        const bool eb = m.c2p == TERM_BAND, fb = m.p2c == TERM_BAND;
-        auto next_first = [&] { if (tn >= 0) load_first(tn, mn); };
         auto q_k = [&](int kb, const uint4 (&kf)[NU]) {
           const f32x16_t c = (m.p2c == TERM_CONST) ? c_init(cjw, kb) : f32x16_t{};
           return mma_chain<T, NU, NC>(kf, qf, c);
@@ -1241,55 +1297,55 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int item, unsigned 
               if (!((kv >> rr_of(r)) & 1u)) acc[r] = NEG_INF;
           }
         };
-        f32x16_t s[2];
         static_assert(C::NKB == 2, "two key halves per tile");
-        // ---- first half: rows E(0,0), E(0,1) then F(0,0), F(0,1) ---------
-        f32x16_t e_keep;
-        {
+        // One 32-key half kb of tile t: its scores (C2C, then the P2C band,
+        // whose K operand dies before the E product, then the C2P band),
+        // then its softmax and P.V. The next half is (t, 1) or (tn, 0).
+        auto half = [&](auto kbc) {
+          constexpr int kb = decltype(kbc)::value;
+          const Modes nm = kb == 0 ? m : mn;
+          const bool has_next = kb == 0 || tn >= 0;
+          const int nt = kb == 0 ? t : tn;
+          constexpr int nkb = kb ^ 1;
+          const bool nadj = kb == 0 || tn == t + 1;
+          const bool eb = m.c2p == TERM_BAND, fb = m.p2c == TERM_BAND;
+          const bool neb = has_next && nm.c2p == TERM_BAND, nfb = has_next && nm.p2c == TERM_BAND;
+          uint4 (&F0B)[NU] = rF[kb];       // this half's F block 0; the next half's block 1
+          uint4 (&F1B)[NU] = rF[kb ^ 1];   // this half's F block 1; the next half's block 0
           uint4 kf[NU];
-          k_operand(ks, 0, kf);
-          f32x16_t acc = q_k(0, kf);
-          if (eb) {
-            const f32x16_t e0 = mma_chain<T, NU, NC>(rw[0], qf, f32x16_t{});
-            const f32x16_t e1 = mma_chain<T, NU, NC>(rw[1], qf, f32x16_t{});
-            e_keep = e0;   // the second half's E block 1
-            if (fb) { load_f(t, 0, 0, rw[0]); load_f(t, 0, 1, rw[1]); }
-            else load_e(t, 1, 0, rw[0]);
-            add_e(e0, e1, acc);
-          }
+          k_operand(ks, kb, kf);
+          f32x16_t acc = q_k(kb, kf);
           if (fb) {
-            const f32x16_t f0 = mma_chain<T, NU, NC>(kf, rw[0], f32x16_t{});
-            if (eb) load_e(t, 1, 0, rw[0]);
-            else load_f(t, 1, 1, rw[0]);
-            // rw[1] stays: its rows are the second half's F block 0
-            const f32x16_t f1 = mma_chain<T, NU, NC>(kf, rw[1], f32x16_t{});
-            add_f(f0, f1, acc);
+            const f32x16_t f0 = mma_chain<T, NU, NC>(kf, F0B, f32x16_t{});
+            if (nfb) load_f(nt, nkb, 1, F0B);
+            const f32x16_t f1 = mma_chain<T, NU, NC>(kf, F1B, f32x16_t{});
+            if (nfb && !nadj) load_f(nt, nkb, 0, F1B);
+            put_f(f0, 0);
+            put_f(f1, 1);
+            sum_f(acc);
+          } else if (nfb) {
+            load_f(nt, nkb, 1, F0B);
+            load_f(nt, nkb, 0, F1B);
           }
-          mask_keys(0, acc);
-          s[0] = acc;
-        }
-        // ---- second half: rows E(1,0) (E(1,1) kept), then F(1,1) ----------
-        {
-          uint4 kf[NU];
-          k_operand(ks, 1, kf);
-          f32x16_t acc = q_k(1, kf);
           if (eb) {
-            const f32x16_t e0 = mma_chain<T, NU, NC>(rw[0], qf, f32x16_t{});
-            if (fb) load_f(t, 1, 1, rw[0]);
-            else next_first();
+            const f32x16_t e0 = mma_chain<T, NU, NC>(rE, qf, f32x16_t{});
+            if (!ek) {
+              // first half of a C2P band run: its E block 1 from its rows now
+              load_e(t, kb, 1, rE);
+              e_keep = mma_chain<T, NU, NC>(rE, qf, f32x16_t{});
+            }
+            if (neb) load_e(nt, nkb, 0, rE);
             add_e(e0, e_keep, acc);
+            e_keep = e0;
+          } else if (neb) {
+            load_e(nt, nkb, 0, rE);
           }
-          if (fb) {
-            const f32x16_t f0 = mma_chain<T, NU, NC>(kf, rw[1], f32x16_t{});
-            const f32x16_t f1 = mma_chain<T, NU, NC>(kf, rw[0], f32x16_t{});
-            next_first();
-            add_f(f0, f1, acc);
-          }
-          if (!eb && !fb) next_first();
-          mask_keys(1, acc);
-          s[1] = acc;
-        }
-        softmax_pv(s, m.a_off, vop_slot(vs));
+          ek = eb && nadj && neb;
+          mask_keys(kb, acc);
+          softmax_pv_half(acc, kb, m.a_off, vop_slot(vs));
+        };
+        half(std::integral_constant<int, 0>{});
+        half(std::integral_constant<int, 1>{});
         t = tn;
         m = mn;
         par ^= 1;
