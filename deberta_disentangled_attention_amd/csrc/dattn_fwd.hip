@@ -850,24 +850,49 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int item, unsigned 
   };
 
   // Online softmax and P.V of one 32-key half of a tile (16-bit types, 16
-  // scores per lane): the same offset rule as softmax_p (raise only past a
-  // margin of 8, detected from the half's maximum); P rounded to the element
-  // type, its row sum taken from the rounded values.
+  // scores per lane): the offset rule of softmax_p (raise only past a margin
+  // of 8); P rounded to the element type, its row sum taken from the rounded
+  // values.
   auto softmax_pv_half = [&](f32x16_t& sv, int kb, float a_off, auto vop) {
     if constexpr (ES == 2) {
       const float tl2 = p.scale_log2;
       const float off = a_off * tl2;
-      float mx4[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
+      typename Ty<T>::frag pf[2];
+      // P = exp2(s tl2 + off - m_run), rounded; returns this lane's sum of it
+      auto exps = [&]() -> float {
+        const float bias = off - (m_run == NEG_INF ? 0.f : m_run);
+        float ps4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int r = 0; r < 16; r += 4) {
-        mx4[0] = fmaxf(mx4[0], sv[r]);
-        mx4[1] = fmaxf(mx4[1], sv[r + 1]);
-        mx4[2] = fmaxf(mx4[2], sv[r + 2]);
-        mx4[3] = fmaxf(mx4[3], sv[r + 3]);
-      }
-      const float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
-      const float mt_half = (mx == NEG_INF) ? NEG_INF : fmaf(mx, tl2, off);
-      if (__builtin_expect(__any(mt_half > m_run + 8.f), 0)) {
+        for (int c2 = 0; c2 < 2; ++c2) {
+          f32x8_t e8;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) e8[e] = __builtin_amdgcn_exp2f(fmaf(sv[8 * c2 + e], tl2, bias));
+          pf[c2] = Ty<T>::cvt8(e8);
+          const uint4 w = __builtin_bit_cast(uint4, pf[c2]);
+          ps4[0] = Ty<T>::sum2(w.x, ps4[0]);
+          ps4[1] = Ty<T>::sum2(w.y, ps4[1]);
+          ps4[2] = Ty<T>::sum2(w.z, ps4[2]);
+          ps4[3] = Ty<T>::sum2(w.w, ps4[3]);
+        }
+        return (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
+      };
+      // Lazy offset: the exponentials are taken against the current m_run;
+      // their sum, at most 16 * 2^8 when no value exceeds m_run by more
+      // than 8, detects a due raise (or an overflow). That rare case, and
+      // a lane with no offset yet, take the cold path: the half's maximum
+      // (both lanes of the query), the raise with its rescale, and the
+      // exponentials again.
+      float ps = exps();
+      if (__builtin_expect(__any(!(ps <= 16.f * 256.f) || m_run == NEG_INF), 0)) {
+        float mx4[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
+#pragma unroll
+        for (int r = 0; r < 16; r += 4) {
+          mx4[0] = fmaxf(mx4[0], sv[r]);
+          mx4[1] = fmaxf(mx4[1], sv[r + 1]);
+          mx4[2] = fmaxf(mx4[2], sv[r + 2]);
+          mx4[3] = fmaxf(mx4[3], sv[r + 3]);
+        }
+        const float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
         const float mxf = fmaxf(mx, wave_xor32(mx));
         const float mt = (mxf == NEG_INF) ? NEG_INF : fmaf(mxf, tl2, off);
         const bool raise = mt > m_run + 8.f;
@@ -878,23 +903,9 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int item, unsigned 
 #pragma unroll
         for (int x = 0; x < C::NDB; ++x) o_acc[x] *= alpha;
         m_run = m_new;
+        ps = exps();
       }
-      const float bias = off - (m_run == NEG_INF ? 0.f : m_run);
-      typename Ty<T>::frag pf[2];
-      float ps4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        f32x8_t e8;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) e8[e] = __builtin_amdgcn_exp2f(fmaf(sv[8 * c2 + e], tl2, bias));
-        pf[c2] = Ty<T>::cvt8(e8);
-        const uint4 w = __builtin_bit_cast(uint4, pf[c2]);
-        ps4[0] = Ty<T>::sum2(w.x, ps4[0]);
-        ps4[1] = Ty<T>::sum2(w.y, ps4[1]);
-        ps4[2] = Ty<T>::sum2(w.z, ps4[2]);
-        ps4[3] = Ty<T>::sum2(w.w, ps4[3]);
-      }
-      l_part += (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
+      l_part += ps;
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
