@@ -3,7 +3,8 @@ prologue (from the work item's start to its first tile: mask or sequence
 search, Q row, relative-table thresholds and window), in the general (band)
 tiles and in the far tiles, and inside the general tiles the split between
 the tile start (load wait and barrier), the score products (C2C, the band
-products E and F and their diagonal gathers) and the softmax with P.V.
+products E and F and their diagonal gathers; both halves) and the softmax with
+P.V (both halves).
 
 It builds a separate library from a copy of the kernel sources with
 s_memtime reads inserted at the phase boundaries; that library's *_lse
@@ -60,14 +61,15 @@ def instrument(src: str) -> str:
     src = _sub(src, "        wait_vm<0>();\n        __syncthreads();  // tile t in its slot; the other slot is free\n",
                f"        pt_ = {stamp};\n"
                "        wait_vm<0>();\n        __syncthreads();  // tile t in its slot; the other slot is free\n")
-    src = _sub(src, "        f32x16_t e_keep;\n",
+    src = _sub(src, "        half(std::integral_constant<int, 0>{});\n",
                f"        {{ const uint64_t tt_ = {stamp}; pc_[4] += (float)(tt_ - pt_); pt_ = tt_; }}\n"
-               "        f32x16_t e_keep;\n")
-    src = _sub(src, "        softmax_pv(s, m.a_off, vop_slot(vs));\n",
-               f"        {{ const uint64_t tt_ = {stamp}; pc_[5] += (float)(tt_ - pt_); pt_ = tt_; }}\n"
-               "        softmax_pv(s, m.a_off, vop_slot(vs));\n"
-               f"        {{ const uint64_t tt_ = {stamp}; pc_[6] += (float)(tt_ - pt_); pt_ = tt_; }}\n"
-               "        pc_[2] += 1.f;\n")
+               "        half(std::integral_constant<int, 0>{});\n")
+    src = _sub(src, "        half(std::integral_constant<int, 1>{});\n",
+               "        half(std::integral_constant<int, 1>{});\n        pc_[2] += 1.f;\n")
+    src = _sub(src, "          mask_keys(kb, acc);\n          softmax_pv_half(acc, kb, m.a_off, vop_slot(vs));\n",
+               f"          {{ const uint64_t tt_ = {stamp}; pc_[5] += (float)(tt_ - pt_); pt_ = tt_; }}\n"
+               "          mask_keys(kb, acc);\n          softmax_pv_half(acc, kb, m.a_off, vop_slot(vs));\n"
+               f"          {{ const uint64_t tt_ = {stamp}; pc_[6] += (float)(tt_ - pt_); pt_ = tt_; }}\n")
     src = _sub(src, "      p.lse[(base + qi) * p.H + head] = row_ok ? (m_run + log2f(l_tot)) * 0.6931471805599453f : NEG_INF;",
                "      { const int kk_ = li & 7; float v_ = 0.f;\n"
                "#pragma unroll\n        for (int z_ = 0; z_ < 8; ++z_) if (kk_ == z_) v_ = pc_[z_];\n"
