@@ -33,10 +33,11 @@
 //    as the accumulator input of the Q.K MFMA;
 //  * band path: per 32-key half, E[u][i] = q_i . kr[T(u)] for the 63
 //    distances u = i - j of the wave and F[j][v] = k_j . qr[T(v)] for the
-//    BM+31 distances v = j - i of the workgroup are produced by MFMA (table
-//    rows gathered into the A/B operands), stored in LDS and read back along
-//    the diagonal. Indexing the bands by distance makes every gather address
-//    a per-lane base plus a compile-time offset.
+//    distances v = j - i (the wave's 63 for 16-bit types, the workgroup's
+//    BM+31 for fp32) are produced by MFMA (table rows gathered into the A/B
+//    operands), stored in LDS and read back along the diagonal. Indexing the
+//    bands by distance makes every gather address a per-lane base plus a
+//    compile-time offset.
 //
 // Masks. The factorised mask m_i m_j: keys with m_j = 0 (or beyond the
 // sequence) get -inf scores and zero V rows; queries with m_i = 0 produce
@@ -1162,8 +1163,9 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int item, unsigned 
 
     // ---- phase 1 (16-bit types): general tiles ------------------------------
     // Tiles with band terms or masked keys. Tile t sits in slot t's parity;
-    // the next general tile is loaded while it is computed. Every band
-    // product is wave-private: per 32-key half, E[u][i] = kr[T(u)] . q_i over
+    // the next general tile is loaded while it is computed. A tile is worked
+    // through per 32-key half, each half with its own softmax and P.V. Every
+    // band product is wave-private: per 32-key half, E[u][i] = kr[T(u)] . q_i over
     // the 63 distances u = i - j of the wave's queries and F[j][v] =
     // k_j . qr[T(v)] over the 63 distances v = j - i are formed by MFMA
     // (table rows gathered into the operands), stored in the wave's LDS
