@@ -141,18 +141,26 @@ __device__ __forceinline__ void lds_half_row(uint4 (&u)[NU], const unsigned char
 
 __device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32); }
 
-// wave-wide integer minimum / maximum; the result is wave-uniform (held
-// in a scalar register)
-__device__ __forceinline__ int wave_min_i(int x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = min(x, __shfl_xor(x, o));
-  return __builtin_amdgcn_readfirstlane(x);
+// Wave-wide integer minimum / maximum by DPP (no LDS traffic): shifts by
+// 1, 2, 4 and 8 lanes within each 16-lane row leave the row's result in its
+// lane 15; row_bcast:15 then carries rows 0 and 2 into rows 1 and 3, and
+// row_bcast:31 carries row 1 into rows 2 and 3, so lane 63 holds the
+// wave's result. Lanes whose DPP source is absent keep the identity. The
+// result is wave-uniform (a scalar register).
+template <bool MAX>
+__device__ __forceinline__ int wave_reduce_i(int x) {
+  constexpr int ID = MAX ? (-2147483647 - 1) : 2147483647;
+  auto op = [](int a, int b) { return MAX ? max(a, b) : min(a, b); };
+  x = op(x, __builtin_amdgcn_update_dpp(ID, x, 0x111, 0xf, 0xf, false));   // row_shr:1
+  x = op(x, __builtin_amdgcn_update_dpp(ID, x, 0x112, 0xf, 0xf, false));   // row_shr:2
+  x = op(x, __builtin_amdgcn_update_dpp(ID, x, 0x114, 0xf, 0xf, false));   // row_shr:4
+  x = op(x, __builtin_amdgcn_update_dpp(ID, x, 0x118, 0xf, 0xf, false));   // row_shr:8
+  x = op(x, __builtin_amdgcn_update_dpp(ID, x, 0x142, 0xa, 0xf, false));   // row_bcast:15
+  x = op(x, __builtin_amdgcn_update_dpp(ID, x, 0x143, 0xc, 0xf, false));   // row_bcast:31
+  return __builtin_amdgcn_readlane(x, 63);
 }
-__device__ __forceinline__ int wave_max_i(int x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = max(x, __shfl_xor(x, o));
-  return __builtin_amdgcn_readfirstlane(x);
-}
+__device__ __forceinline__ int wave_min_i(int x) { return wave_reduce_i<false>(x); }
+__device__ __forceinline__ int wave_max_i(int x) { return wave_reduce_i<true>(x); }
 
 // Direct-to-LDS load (global_load_lds_dwordx4): lane i's 16 bytes at
 // gbase + voff are written to LDS byte address lds + 16 i. The data bypasses
