@@ -42,7 +42,10 @@ def run_padded(w: workloads.Workload, rel_max_len=None, flags=None, scale=0.0, m
     T = (gpu_table(rel_max_len, w.position_buckets, w.max_relative_positions) if table is None
          else torch.from_numpy(np.ascontiguousarray(table, np.int32)).cuda())
     mask = w.mask if mask is None else mask
-    m = None if mask is None else torch.from_numpy(np.ascontiguousarray(mask, np.uint8)).cuda()
+    if isinstance(mask, torch.Tensor):
+        m = mask   # a device tensor, passed as it is (its address included)
+    else:
+        m = None if mask is None else torch.from_numpy(np.ascontiguousarray(mask, np.uint8)).cuda()
     out = dd.dattn_fwd_padded(q if q is not None else dev(w.q, w.dtype),
                               k if k is not None else dev(w.k, w.dtype),
                               v if v is not None else dev(w.v, w.dtype),

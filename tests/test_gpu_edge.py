@@ -344,3 +344,32 @@ def test_far_offset_raises_mid_run(dtype, packed):
     _say(f"far offset raises {dtype} packed={packed}: max abs err {err:.3e}")
     assert np.all(np.isfinite(got))
     assert err <= H.TOL[dtype], err
+
+
+def test_mask_scan_batches_and_alignment():
+    """The padded extent scan reads the mask in batches (2048 positions a
+    batch by 4-byte words, 512 by bytes when the row length or the pointer is
+    not word-aligned): the last valid position and the first padded one lie
+    past the first batch here, in both forms, and the same mask at an odd
+    address (byte form) gives the word form's output bit for bit."""
+    import torch
+    for L, dtype in ((2600, "bf16"), (1001, "fp16")):
+        w = workloads.make_workload(f"scan{L}", dtype=dtype, B=2, L=L, H=1, d=64,
+                                    position_buckets=256, max_relative_positions=512,
+                                    lens=np.array([L, L]), seed=11)
+        m = np.zeros((2, L), np.uint8)
+        m[0, :L - 200] = 1
+        m[0, L - 700] = 0                # first padded position past the first batch
+        m[1, :5] = 1
+        m[1, L - 10] = 1                 # last valid position past the first batch
+        w.mask = m
+        _say(f"mask scan L={L} {dtype}")
+        got = H.host(H.run_padded(w))
+        want = H.oracle_padded(w)
+        H.assert_padded_close(got, want, m.astype(bool), dtype, f"mask scan L={L}")
+        big = torch.zeros(2 * L + 1, dtype=torch.uint8, device="cuda")
+        big[1:] = torch.from_numpy(m.reshape(-1)).cuda()
+        odd = big[1:].view(2, L)
+        assert odd.data_ptr() % 4 != 0
+        got_odd = H.host(H.run_padded(w, mask=odd))
+        assert np.array_equal(got, got_odd)
