@@ -1228,9 +1228,28 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int item, unsigned 
         const int umin = i0w - (t * BN + 32 * kb + 31);
         load_half_row<NU>(dst, krb + (rel_off(umin + 32 * ub + li, twok) + lhb));
       };
+      // F products as 16x16x32 MFMAs (d <= 64: three quarters of the 32x32
+      // work, the two 16x16 corners no pair reaches skipped) or as two 32x32
+      // chains (d = 128, where the longer 16x16 chains measured slower).
+      // 16x16 form: F rows in the B-operand layout, F block vb (32
+      // distances) is two 16-distance blocks bb, lane l holding the row of
+      // distance 16 bb + l % 16 and, for each of the D / 32 k-steps m, its
+      // 16-byte unit 4 m + l / 16 (dst[KS16 bb + m])
+      constexpr bool F16 = D <= 64;
+      constexpr int KS16 = D / 32;
+      static_assert(2 * KS16 == NU, "two 16-distance blocks fill an F buffer");
       auto load_f = [&](int t, int kb, int vb, uint4 (&dst)[NU]) {
         const int vmin = (t * BN + 32 * kb) - (i0w + 31);
-        load_half_row<NU>(dst, qrb + (rel_off(vmin + 32 * vb + li, twok) + lhb));
+        if constexpr (F16) {
+#pragma unroll
+          for (int bb = 0; bb < 2; ++bb) {
+            const unsigned char* row = qrb + rel_off(vmin + 32 * vb + 16 * bb + (lane & 15), twok);
+#pragma unroll
+            for (int m = 0; m < KS16; ++m) dst[KS16 * bb + m] = ld16(row + 16 * (4 * m + (lane >> 4)));
+          }
+        } else {
+          load_half_row<NU>(dst, qrb + (rel_off(vmin + 32 * vb + li, twok) + lhb));
+        }
       };
       // E[u][i] (two 32-distance blocks) into the scratch, then added along
       // the diagonal; likewise F[j][v]. The scratch is rewritten only after
@@ -1243,10 +1262,38 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int item, unsigned 
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[r] += e_rd[(27 - rr_of(r)) * 32];
       };
-      // F block vb into the scratch; then its diagonal added
+      // 32x32 form: F block vb into the scratch; then its diagonal added
       auto put_f = [&](const f32x16_t& f, int vb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) scr[(rr_of(r) + 4 * lh) * 64 + 32 * vb + li] = f[r];
+      };
+      // 16x16 form: F[j][v] of key half kb: 16x16x32 products of key sub-block s (keys
+      // 16 s + 0..15, A operand from the K tile) with the 16-distance blocks
+      // b = s .. s + 2 its pairs reach (the half's F blocks 0 and 1 hold
+      // b = 0, 1 and 2, 3), each stored in the scratch as it completes
+      auto f_products = [&](const unsigned char* ks, int kb, const uint4 (&fb0)[NU],
+                            const uint4 (&fb1)[NU]) {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+          const int r = 32 * kb + 16 * sb + (lane & 15);
+          typename Ty<T>::frag ka[KS16];
+#pragma unroll
+          for (int m = 0; m < KS16; ++m)
+            ka[m] = __builtin_bit_cast(typename Ty<T>::frag,
+                                       ld16(ks + r * ROWB + 16 * ((4 * m + (lane >> 4)) ^ C::swz_k(r))));
+#pragma unroll
+          for (int b = sb; b < sb + 3; ++b) {
+            f32x4_t acc = f32x4_t{};
+#pragma unroll
+            for (int m = 0; m < KS16; ++m) {
+              const uint4 bq = b < 2 ? fb0[KS16 * b + m] : fb1[KS16 * (b - 2) + m];
+              acc = Ty<T>::mma16(ka[m], __builtin_bit_cast(typename Ty<T>::frag, bq), acc);
+            }
+            // lane l holds distance 16 b + l % 16 of keys 16 sb + 4 (l / 16) + 0..3
+#pragma unroll
+            for (int i = 0; i < 4; ++i) scr[(16 * sb + 4 * (lane >> 4) + i) * 64 + 16 * b + (lane & 15)] = acc[i];
+          }
+        }
       };
       auto sum_f = [&](f32x16_t& acc) {
 #pragma unroll
@@ -1329,12 +1376,18 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int item, unsigned 
           k_operand(ks, kb, kf);
           f32x16_t acc = q_k(kb, kf);
           if (fb) {
-            const f32x16_t f0 = mma_chain<T, NU, NC>(kf, F0B, f32x16_t{});
-            if (nfb) load_f(nt, nkb, 1, F0B);
-            const f32x16_t f1 = mma_chain<T, NU, NC>(kf, F1B, f32x16_t{});
-            if (nfb && !nadj) load_f(nt, nkb, 0, F1B);
-            put_f(f0, 0);
-            put_f(f1, 1);
+            if constexpr (F16) {
+              f_products(ks, kb, F0B, F1B);
+              if (nfb) load_f(nt, nkb, 1, F0B);
+              if (nfb && !nadj) load_f(nt, nkb, 0, F1B);
+            } else {
+              const f32x16_t f0 = mma_chain<T, NU, NC>(kf, F0B, f32x16_t{});
+              if (nfb) load_f(nt, nkb, 1, F0B);
+              const f32x16_t f1 = mma_chain<T, NU, NC>(kf, F1B, f32x16_t{});
+              if (nfb && !nadj) load_f(nt, nkb, 0, F1B);
+              put_f(f0, 0);
+              put_f(f1, 1);
+            }
             sum_f(acc);
           } else if (nfb) {
             load_f(nt, nkb, 1, F0B);
