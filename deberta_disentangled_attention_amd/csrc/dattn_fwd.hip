@@ -112,7 +112,10 @@ struct Cfg {
   // general tiles of 16-bit types: two slots of the ring's layout, then the
   // per-wave scratch of the band products (E: 64 distances x 32 queries, F:
   // 32 keys x 64 distances, fp32) and of the per-wave c_j
-  static constexpr int SCR_BYTES = 64 * 32 * 4;
+  // F rows are FPITCH floats apart: the 16x16 products store four key rows
+  // 4 apart per instruction, which then fall 16 banks apart
+  static constexpr int FPITCH = 68;
+  static constexpr int SCR_BYTES = (64 * 32 > 32 * FPITCH ? 64 * 32 : 32 * FPITCH) * 4;
   static constexpr int OFF_SCR = 2 * SLOT_BYTES;
   static constexpr int OFF_CJW = OFF_SCR + NW * SCR_BYTES;
   static constexpr int G16_BYTES = ES == 2 ? OFF_CJW + NW * BN * 4 : 0;
@@ -1177,7 +1180,8 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int item, unsigned 
       float* scr = reinterpret_cast<float*>(smem + C::OFF_SCR + wave * C::SCR_BYTES);
       float* cjw = reinterpret_cast<float*>(smem + C::OFF_CJW + wave * BN * 4);
       const float* e_rd = scr + (li + 4 - 4 * lh) * 32 + li;   // + (27 - rr) * 32
-      const float* f_rd = scr + 4 * lh * 65 + 31 - li;         // + rr * 65
+      constexpr int FP = C::FPITCH;
+      const float* f_rd = scr + 4 * lh * (FP + 1) + 31 - li;   // + rr * (FP + 1)
       struct Modes { int c2p, p2c, which; float a_off; };
       // paths of the two terms over this wave's pairs with tile t
       auto wave_modes = [&](int t) {
@@ -1265,7 +1269,7 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int item, unsigned 
       // 32x32 form: F block vb into the scratch; then its diagonal added
       auto put_f = [&](const f32x16_t& f, int vb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) scr[(rr_of(r) + 4 * lh) * 64 + 32 * vb + li] = f[r];
+        for (int r = 0; r < 16; ++r) scr[(rr_of(r) + 4 * lh) * FP + 32 * vb + li] = f[r];
       };
       // 16x16 form: F[j][v] of key half kb: 16x16x32 products of key sub-block s (keys
       // 16 s + 0..15, A operand from the K tile) with the 16-distance blocks
@@ -1291,13 +1295,13 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int item, unsigned 
             }
             // lane l holds distance 16 b + l % 16 of keys 16 sb + 4 (l / 16) + 0..3
 #pragma unroll
-            for (int i = 0; i < 4; ++i) scr[(16 * sb + 4 * (lane >> 4) + i) * 64 + 16 * b + (lane & 15)] = acc[i];
+            for (int i = 0; i < 4; ++i) scr[(16 * sb + 4 * (lane >> 4) + i) * FP + 16 * b + (lane & 15)] = acc[i];
           }
         }
       };
       auto sum_f = [&](f32x16_t& acc) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] += f_rd[rr_of(r) * 65];
+        for (int r = 0; r < 16; ++r) acc[r] += f_rd[rr_of(r) * (FP + 1)];
       };
 
       int t = first_general;
