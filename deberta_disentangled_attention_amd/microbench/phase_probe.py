@@ -14,6 +14,12 @@ log-sum-exp. The product library is not touched.
 
     python -m deberta_disentangled_attention_amd.microbench.phase_probe build
     python -m deberta_disentangled_attention_amd.microbench.phase_probe run c4 c4l2048 c2
+
+With --split (on both commands, its own library) two counters change meaning:
+the far-step count becomes the general tiles' wait for their loads alone
+(before the barrier), and the prologue becomes the P2C block of the general
+tiles (its products, next-row fetches and diagonal sums), both in cycles per
+general tile.
 """
 
 from __future__ import annotations
@@ -30,11 +36,18 @@ from .. import build as B
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC_DIR = os.path.join(HERE, "bin", "phase_src")
 LIB = os.path.join(HERE, "bin", "libdattn_phase.so")
+SPLIT = "--split" in sys.argv
+if SPLIT:
+    SRC_DIR = os.path.join(HERE, "bin", "phase_split_src")
+    LIB = os.path.join(HERE, "bin", "libdattn_phase_split.so")
 ROOT = os.path.dirname(B.PKG_DIR)
 
 COUNTERS = ["general tiles, all", "far tiles, all", "general tiles (count)", "far steps (count)",
             "general: start (wait, barrier, loads issue)", "general: score products",
             "general: softmax + P.V", "prologue"]
+if SPLIT:
+    COUNTERS[3] = "general: load wait only"
+    COUNTERS[7] = "general: P2C block"
 
 
 def _sub(text: str, anchor: str, new: str) -> str:
@@ -74,6 +87,16 @@ def instrument(src: str) -> str:
                "      { const int kk_ = li & 7; float v_ = 0.f;\n"
                "#pragma unroll\n        for (int z_ = 0; z_ < 8; ++z_) if (kk_ == z_) v_ = pc_[z_];\n"
                "        p.lse[(base + qi) * p.H + head] = v_; }")
+    if SPLIT:
+        src = _sub(src, "    pc_[3] += (float)nfar;\n", "")
+        src = _sub(src, "    pc_[7] = (float)(pg0_ - pe_);\n", "")
+        src = _sub(src, "        wait_vm<0>();\n        __syncthreads();  // tile t in its slot",
+                   f"        wait_vm<0>();\n        {{ const uint64_t tw_ = {stamp}; pc_[3] += (float)(tw_ - pt_); }}\n"
+                   "        __syncthreads();  // tile t in its slot")
+        src = _sub(src, "          if (fb) {\n            if constexpr (F16) {",
+                   f"          const uint64_t tf_ = {stamp};\n          if (fb) {{\n            if constexpr (F16) {{")
+        src = _sub(src, "          if (eb) {\n            const f32x16_t e0",
+                   f"          pc_[7] += (float)({stamp} - tf_);\n          if (eb) {{\n            const f32x16_t e0")
     return src
 
 
@@ -150,6 +173,8 @@ def run(workloads) -> None:
         per_g = lambda x: float(np.mean(x[live] / c[2][live])) if live.any() else 0.0
         vals = [np.mean(c[0]), np.mean(c[1]), np.mean(c[2]), np.mean(c[3]), per_g(c[4]), per_g(c[5]),
                 per_g(c[6]), np.mean(c[7])]
+        if SPLIT:
+            vals[3], vals[7] = per_g(c[3]), per_g(c[7])
         print(f"| {name} | " + " | ".join(f"{x:.0f}" if i not in (2, 3) else f"{x:.1f}"
                                             for i, x in enumerate(vals)) + " |", flush=True)
     print("\nTotals and the prologue are cycles per wave (s_memtime); the three general-tile parts are"
@@ -157,9 +182,10 @@ def run(workloads) -> None:
 
 
 if __name__ == "__main__":
-    if len(sys.argv) < 2 or sys.argv[1] not in ("build", "run"):
+    args = [a for a in sys.argv[1:] if a != "--split"]
+    if not args or args[0] not in ("build", "run"):
         raise SystemExit(__doc__)
-    if sys.argv[1] == "build":
+    if args[0] == "build":
         build()
     else:
-        run(sys.argv[2:] or ["c4"])
+        run(args[1:] or ["c4"])
