@@ -44,7 +44,9 @@ METRIC = "effective TFLOP/s + tokens/s, disentangled attn fwd, bf16 d=64, % MFMA
 PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}   # MI355X dense MFMA
 HBM_GBS = 8000.0
 KERNEL_SOURCES = ["deberta_disentangled_attention_amd/csrc/dattn_fwd.hip",
-                  "deberta_disentangled_attention_amd/csrc/dattn_device.h"]
+                  "deberta_disentangled_attention_amd/csrc/dattn_fwd_d128.hip",
+                  "deberta_disentangled_attention_amd/csrc/dattn_device.h",
+                  "deberta_disentangled_attention_amd/build.py"]   # its flags shape the kernel too
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dattn_fwd_c4_bf16_traffic.json")
 
 

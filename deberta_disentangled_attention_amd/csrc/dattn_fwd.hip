@@ -1799,6 +1799,18 @@ constexpr bool kNwForced = false;
 #endif
 constexpr int kShortPackedLen = 128;   // packed, max_seqlen up to this: 64-query tiles
 
+// The fp16/bf16 d = 128 instances live in a unit of their own
+// (dattn_fwd_d128.hip, which includes this file with the macro below set),
+// compiled with another machine scheduler than the rest.
+int launch_fwd_h16_d128(FwdParams& p, bool fp16, bool varlen, hipStream_t stream)
+#ifdef DATTN_FWD_H16_D128_UNIT
+{
+  if (fp16) return launch_inst<TF16, 128, 64, DATTN_NW_D128>(p, varlen, stream);
+  return launch_inst<TBF16, 128, 64, DATTN_NW_D128>(p, varlen, stream);
+}
+#else
+;
+
 template <class T>
 int launch_dtype(FwdParams& p, int d, bool varlen, hipStream_t stream) {
   constexpr bool h16 = Ty<T>::ESIZE == 2;
@@ -1819,7 +1831,7 @@ int launch_dtype(FwdParams& p, int d, bool varlen, hipStream_t stream) {
         return launch_inst<T, 64, 64, 4>(p, varlen, stream);
       }
     case 128:
-      if constexpr (h16) return launch_inst<T, 128, 64, DATTN_NW_D128>(p, varlen, stream);
+      if constexpr (h16) return launch_fwd_h16_d128(p, std::is_same<T, TF16>::value, varlen, stream);
       else return launch_inst<T, 128, 32, 4>(p, varlen, stream);
     default: return 2;
   }
@@ -1833,5 +1845,6 @@ int launch_fwd(FwdParams& p, int dtype, int d, bool varlen, hipStream_t stream) 
     default: return 2;
   }
 }
+#endif  // DATTN_FWD_H16_D128_UNIT
 
 }  // namespace dattn

@@ -115,7 +115,7 @@ def build() -> str:
 
     def cc(pair):
         s, o = pair
-        subprocess.run([B.hipcc(), *flags, "-c", "-o", o, os.path.join(SRC_DIR, s)], check=True)
+        subprocess.run([B.hipcc(), *flags, *B.source_flags(s), "-c", "-o", o, os.path.join(SRC_DIR, s)], check=True)
 
     with ThreadPoolExecutor(8) as ex:
         list(ex.map(cc, zip(B.SOURCES, objs)))
