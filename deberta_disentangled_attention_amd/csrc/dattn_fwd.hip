@@ -1271,10 +1271,11 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int item, unsigned 
 #pragma unroll
         for (int r = 0; r < 16; ++r) scr[(rr_of(r) + 4 * lh) * FP + 32 * vb + li] = f[r];
       };
-      // 16x16 form: F[j][v] of key half kb: 16x16x32 products of key sub-block s (keys
-      // 16 s + 0..15, A operand from the K tile) with the 16-distance blocks
-      // b = s .. s + 2 its pairs reach (the half's F blocks 0 and 1 hold
-      // b = 0, 1 and 2, 3), each stored in the scratch as it completes
+      // 16x16 form: F[j][v] of key half kb: 16x16x32 products of key
+      // sub-block sb (keys 16 sb + 0..15, A operand from the K tile) with the
+      // 16-distance blocks b = sb .. sb + 2 its pairs reach (the half's F
+      // blocks 0 and 1 hold b = 0, 1 and 2, 3), each stored in the scratch
+      // as it completes
       auto f_products = [&](const unsigned char* ks, int kb, const uint4 (&fb0)[NU],
                             const uint4 (&fb1)[NU]) {
 #pragma unroll
