@@ -1569,9 +1569,33 @@ __device__ __forceinline__ void fwd_item(const FwdParams& p, int item, unsigned 
         // unconditional, so the MFMAs share a block with the exponentials;
         // past the last tile of a run they read a slot whose result is not
         // used
-        scores(n + 1, qop, s_nxt);
+        // d <= 64 (built with the max-ilp scheduler): tile n+1's K operand is
+        // read from LDS first, ahead of a scheduling barrier, so the Q.K
+        // MFMAs find it in registers; max-ilp would otherwise issue each
+        // read just before its MFMA and expose the LDS latency there. The
+        // group hints then spread the exponentials over the MFMAs: per MFMA
+        // two exponentials and one other VALU instruction. (d = 128, built
+        // with the default scheduler, ran 4-5% slower with both.)
+        constexpr bool PIN_K = D <= 64;
+        if constexpr (PIN_K) {
+          uint4 kf_n[C::NKB][NU];
+#pragma unroll
+          for (int kb = 0; kb < C::NKB; ++kb) k_operand(kslot(n + 1), kb, kf_n[kb]);
+          __builtin_amdgcn_sched_barrier(0);
+          scores_from(kf_n, qop, s_nxt);
+        } else {
+          scores(n + 1, qop, s_nxt);
+        }
         pv_acc(pf_prev, s_cur, vop_slot(vslot(n + VS - 1)));   // tile n-1
         float ps = exps(s_cur, pf_cur, std::false_type{}, 0.f);
+        if constexpr (PIN_K) {
+#pragma unroll
+          for (int g = 0; g < 2 * C::NKB * NU; ++g) {   // the step's MFMA count
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x400, 2, 0);   // two transcendental
+            __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);   // one VALU
+          }
+        }
         bool raised = false;
         if (__builtin_expect(__any(!(ps <= 32.f * 256.f) || m_run == NEG_INF), 0)) {
           scores_global(n, qop, s_cur);
